@@ -1,0 +1,259 @@
+"""Throughput of one paged-attention decode step on one MI355X.
+
+A step is the whole hot path over one batch: pa_cache_write of each
+sequence's new token, then attention over every sequence's paged cache
+(pa_decode_partitioned + pa_reduce, or the single-pass pa_decode; both are
+timed and the faster is reported, with its name).  Inputs are seeded
+synthetic batches (see paged_kv_cache_222_amd/workloads.py); the default is
+the LLaMA-3-8B-shaped GQA batch (B=128, 32/8 heads, d128, bf16, log-normal
+context lengths).  Several copies of the inputs are resident in HBM and the
+steps rotate over them, so no step finds the previous step's K/V in the
+256 MB last-level cache.
+
+Prints one JSON line: KV-read GB/s (value), seq-steps/s, fraction of the
+8 TB/s HBM peak, the dominant kernel's roofline figures from HIP events, and
+the fp64 CPU oracle timed on a bounded sample of the same batch.
+"""
+
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0
+METRIC = ("paged-attn decode KV-read GB/s (% of 8 TB/s HBM peak) and "
+          "seq-steps/s")
+
+
+def log(msg):
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=100)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--config", default="llama3-8b")
+    ap.add_argument("--seed", type=int, default=0)
+    ap.add_argument("--block-size", type=int, default=None)
+    ap.add_argument("--partition-size", type=int, default=None)
+    ap.add_argument("--copies", type=int, default=3,
+                    help="resident input copies the steps rotate over")
+    ap.add_argument("--variant", choices=["best", "partitioned", "single"],
+                    default="best")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0,
+                    help="budget of the CPU oracle sample")
+    return ap.parse_args()
+
+
+def algorithmic_bytes(w):
+    """Bytes the attention kernel must move per launch (its roofline unit is
+    one sequence-step): every cached K/V row of every KV head, the queries,
+    the used block-table entries and the context lengths."""
+    c = w.cfg
+    nb = {"f32": 4, "f16": 2, "bf16": 2}[c.dtype]
+    kv = w.kv_bytes_logical()
+    q = c.batch * c.n_q_heads * c.d_head * nb
+    tbl = 4 * int((-(-w.context_lens.astype(np.int64) // c.block_size)).sum())
+    return kv + q + tbl + 4 * c.batch
+
+
+def cpu_baseline(w, budget_s):
+    """The fp64 oracle on the host cores, over the first sequences of the
+    batch (all query heads) until the time budget is spent."""
+    import oracle
+    c = w.cfg
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()]
+                      or [1])
+    except Exception:  # noqa: BLE001
+        threads = 1
+    k_ref, v_ref = oracle.oracle_cache_write(w.k_pool, w.v_pool, w.key_new,
+                                             w.value_new, w.slot_mapping,
+                                             c.block_size)
+    nbytes = {"f32": 4, "f16": 2, "bf16": 2}[c.dtype]
+    t0 = time.perf_counter()
+    done, kv = 0, 0
+    for b in range(c.batch):
+        oracle.oracle_decode(w.q, k_ref, v_ref, w.block_table, w.context_lens,
+                             w.scale, c.gqa_group, c.block_size, c.dtype,
+                             rows=[(b, h) for h in range(c.n_q_heads)])
+        done += 1
+        kv += int(w.context_lens[b]) * c.n_kv_heads * c.d_head * 2 * nbytes
+        if time.perf_counter() - t0 > budget_s:
+            break
+    dt = time.perf_counter() - t0
+    return {"value": round(kv / dt / 1e9, 4), "unit": "GB/s",
+            "seq_steps_per_s": round(done / dt, 3), "cores": int(threads),
+            "host_cpus": len(os.sched_getaffinity(0)), "kind": "oracle",
+            "sample": f"first {done} of {c.batch} sequences, all "
+                      f"{c.n_q_heads} query heads, fp64 numpy, {dt:.1f} s"}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only; --gpus {args.gpus} is not "
+              "supported (the decode path shards by sequence or KV head with "
+              "no exchange, so N GPUs would run N independent copies)",
+              file=sys.stderr)
+        sys.exit(2)
+    import torch
+
+    import paged_kv_cache_222_amd as pa
+    from paged_kv_cache_222_amd import workloads as wl
+
+    if not torch.cuda.is_available():
+        sys.exit("bench.py needs a GPU")
+    pa.load()
+    kw = {}
+    if args.block_size:
+        kw["block_size"] = args.block_size
+    t = time.perf_counter()
+    w = wl.make_workload(args.config, seed=args.seed, **kw)
+    c = w.cfg
+    P = args.partition_size or c.partition_size
+    pmax = max(1, -(-int(w.context_lens.max()) // P))
+    log(f"generated {c.name} in {time.perf_counter() - t:.1f}s: B={c.batch} "
+        f"Hq={c.n_q_heads} Hkv={c.n_kv_heads} D={c.d_head} BS={c.block_size} "
+        f"{c.dtype} sum(ctx)={int(w.context_lens.sum())} P={P} PMAX={pmax}")
+
+    tdt = {"f32": torch.float32, "f16": torch.float16,
+           "bf16": torch.bfloat16}[c.dtype]
+
+    def up(x, dt=None):
+        if dt == torch.bfloat16:
+            return torch.from_numpy(x.view(np.int16)).view(tdt).cuda()
+        return torch.from_numpy(np.ascontiguousarray(x)).cuda()
+
+    copies = []
+    for i in range(args.copies):
+        copies.append(dict(k=up(w.k_pool, tdt), v=up(w.v_pool, tdt),
+                           q=up(w.q, tdt), kn=up(w.key_new, tdt),
+                           vn=up(w.value_new, tdt)))
+    tbl, cl, slots = up(w.block_table), up(w.context_lens), up(w.slot_mapping)
+    out = torch.empty_like(copies[0]["q"])
+    ws = pa.partition_workspace(c.batch, c.n_q_heads, c.d_head, pmax)
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+
+    def step(x, variant, ev=None):
+        if ev is not None:
+            ev[0].record(stream)
+        pa.pa_cache_write(x["kn"], x["vn"], x["k"], x["v"], slots)
+        if ev is not None:
+            ev[1].record(stream)
+        if variant == "single":
+            pa.pa_decode(out, x["q"], x["k"], x["v"], tbl, cl, scale=w.scale)
+            if ev is not None:
+                ev[2].record(stream)
+        else:
+            pa.pa_decode_partitioned(*ws, x["q"], x["k"], x["v"], tbl, cl,
+                                     partition_size=P, scale=w.scale)
+            if ev is not None:
+                ev[2].record(stream)
+            pa.pa_reduce(out, *ws, cl, partition_size=P)
+        if ev is not None:
+            ev[3].record(stream)
+
+    def timed(variant):
+        for i in range(args.warmup):
+            step(copies[i % len(copies)], variant)
+        torch.cuda.synchronize()
+        # the timed region: exactly --steps steps, nothing else
+        t0 = time.perf_counter()
+        for i in range(args.steps):
+            step(copies[i % len(copies)], variant)
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - t0
+        # the same steps again with events around each kernel
+        evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)]
+               for _ in range(args.steps)]
+        for i in range(args.steps):
+            step(copies[i % len(copies)], variant, evs[i])
+        torch.cuda.synchronize()
+        per = np.array([[e[0].elapsed_time(e[1]), e[1].elapsed_time(e[2]),
+                         e[2].elapsed_time(e[3]), e[0].elapsed_time(e[3])]
+                        for e in evs]) * 1e3   # microseconds
+        return wall, per
+
+    variants = (["partitioned", "single"] if args.variant == "best"
+                else [args.variant])
+    results = {}
+    for v in variants:
+        log(f"timing {v}: warmup {args.warmup}, steps {args.steps}")
+        wall, per = timed(v)
+        results[v] = (wall, per)
+        log(f"{v}: {wall / args.steps * 1e3:.4f} ms/step wall; kernel us "
+            f"write {per[:, 0].mean():.1f} attn {per[:, 1].mean():.1f} "
+            f"reduce {per[:, 2].mean():.1f}")
+    best = min(results, key=lambda v: results[v][0])
+    wall, per = results[best]
+    ms = wall / args.steps * 1e3
+    kv = w.kv_bytes_logical()
+    uniq = w.kv_bytes_unique() if c.prefix_len else kv
+    gbs = kv / (ms * 1e-3) / 1e9
+    attn_us = float(per[:, 1].mean())
+    alg = algorithmic_bytes(w)
+    if c.prefix_len:
+        alg = alg - kv + uniq
+    achieved = alg / (attn_us * 1e-6) / 1e9
+    kernel = ("attention_kernel (pa_decode_partitioned)" if best ==
+              "partitioned" else "attention_kernel (pa_decode)")
+    rec = {
+        "metric": METRIC,
+        "value": round(gbs, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": c.dtype,
+        "data": "synthetic",
+        "config": {"workload": f"{c.name} decode step (cache write + "
+                               f"attention), one layer: {c.description}",
+                   "batch": c.batch, "n_q_heads": c.n_q_heads,
+                   "n_kv_heads": c.n_kv_heads, "d_head": c.d_head,
+                   "block_size": c.block_size, "partition_size": P,
+                   "sum_context": int(w.context_lens.sum()),
+                   "seed": args.seed, "variant": best},
+        "seq_steps_per_s": round(c.batch / (ms * 1e-3), 1),
+        "pct_of_hbm_peak": round(100 * (uniq / (ms * 1e-3) / 1e9)
+                                 / HBM_PEAK_GBS, 2),
+        "kv_bytes_per_step": kv,
+        "kv_bytes_unique_per_step": uniq,
+        "kernel_us": {"cache_write": round(float(per[:, 0].mean()), 2),
+                      "attention": round(attn_us, 2),
+                      "reduce": round(float(per[:, 2].mean()), 2),
+                      "step_events": round(float(per[:, 3].mean()), 2)},
+        "variants_ms_per_step": {v: round(results[v][0] / args.steps * 1e3, 5)
+                                 for v in results},
+        "roofline": {"kernel": kernel, "bound": "hbm",
+                     "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
+                     "traffic": None,
+                     "algorithmic_bytes_per_launch": alg,
+                     "avg_launch_us": round(attn_us, 3)},
+    }
+    if not args.no_cpu_baseline:
+        log("timing the fp64 CPU oracle on a sample")
+        rec["cpu_baseline"] = cpu_baseline(w, args.cpu_seconds)
+    print(json.dumps(rec), flush=True)
+
+
+if __name__ == "__main__":
+    main()

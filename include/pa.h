@@ -1,0 +1,162 @@
+/*
+ * pa.h -- paged KV-cache decode attention for AMD MI355X (gfx950).
+ *
+ * The method: the KV cache of every sequence lives in fixed-size blocks of
+ * block_size token positions scattered through one pool, and a per-sequence
+ * block table maps logical positions to physical blocks ("Serving"
+ * (transformers-and-math module 23), section 23.4 Paged Attention; the
+ * "Paged Attention: Managing the KV Cache Like Virtual Memory" summary on the
+ * inference-serving tag page).  A decode step writes each sequence's new
+ * token into its slot, then reads the whole cached K/V of every sequence for
+ * one query token per sequence ("Serving", section 23.2 Prefill and Decode).
+ * The attention is scaled dot-product softmax attention; grouped-query
+ * attention lets gqa_group consecutive query heads share one KV head
+ * ("Serving", section 23.1: 8 KV heads for 32 query heads in LLaMA-3 8B).
+ *
+ * Conventions for every entry point
+ * ---------------------------------
+ * - Pointers are DEVICE pointers owned by the caller unless stated otherwise.
+ *   The library never allocates, frees or retains memory and keeps no state
+ *   between calls, so calls on different streams are independent.
+ * - All arrays are dense and row-major, with the shapes given below, and
+ *   every array pointer is 16-byte aligned.
+ * - q, pools and out share one element type (dtype); partition workspace is
+ *   always float32.  Accumulation is float32; outputs are rounded to dtype
+ *   with round-to-nearest-even.
+ * - Pool layout: [n_blocks, n_kv_heads, block_size, d_head].  Position t of
+ *   sequence b lives in block block_table[b * max_blocks + t / block_size] at
+ *   offset t % block_size.  Flat slot of a position: block * block_size +
+ *   offset.
+ * - Supported: d_head in {64, 128}; block_size in {8, 16, 32, 64} (a power of
+ *   two, multiple of 8); dtype PA_F32, PA_F16, PA_BF16; gqa_group >= 1.
+ * - Each call checks its host-side arguments, enqueues its kernels on
+ *   `stream` (a hipStream_t; NULL = the default stream) and returns without
+ *   waiting.  Calls on one stream run in order, so a cache write followed by
+ *   a decode on the same stream sees the written token.
+ * - Return value: PA_OK, or a negative status (pa_strerror gives text).  A
+ *   failed argument check enqueues nothing.  PA_ERR_HIP reports a launch
+ *   error; faults inside a kernel surface at the caller's next sync.
+ * - Contract violations found on the device never cause out-of-bounds
+ *   accesses: a sequence whose context length is negative or exceeds
+ *   max_blocks * block_size (or the workspace), or whose table names a block
+ *   outside [0, n_blocks) for a used position, gets NaN in every output
+ *   element of that sequence; a cache-write slot outside
+ *   [0, n_blocks * block_size) is skipped.
+ * - batch == 0 (or n_tokens == 0) is a no-op returning PA_OK.
+ */
+#ifndef PA_H_
+#define PA_H_
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum pa_dtype {
+  PA_F32 = 0,  /* IEEE binary32 */
+  PA_F16 = 1,  /* IEEE binary16 */
+  PA_BF16 = 2  /* bfloat16 (upper half of a binary32) */
+} pa_dtype;
+
+enum {
+  PA_OK = 0,
+  PA_ERR_NULL = -1,        /* a required pointer is NULL */
+  PA_ERR_SHAPE = -2,       /* a size is negative or inconsistent */
+  PA_ERR_UNSUPPORTED = -3, /* d_head, block_size or dtype not supported */
+  PA_ERR_WORKSPACE = -4,   /* max_partitions < 1 */
+  PA_ERR_PARTITION = -5,   /* partition_size not a positive multiple of block_size */
+  PA_ERR_HIP = -6,         /* the HIP runtime reported an error at launch */
+  PA_ERR_ALIGN = -7        /* an array pointer is not 16-byte aligned */
+};
+
+/*
+ * pa_cache_write -- put each new token's key and value into its pool slot.
+ *
+ * The cache grows token by token into blocks allocated as the sequence grows
+ * ("Serving", section 23.4).  For i < n_tokens with s = slot_mapping[i]:
+ *   k_pool[s / block_size, h, s % block_size, :] = key[i, h, :]   for all h
+ *   v_pool[...]                                  = value[i, h, :]
+ * A bit copy (no rounding).  s < 0 skips token i.  Slots must be distinct;
+ * with duplicates the surviving value is unspecified.
+ *
+ *   key, value     [n_tokens, n_kv_heads, d_head]           dtype, read
+ *   k_pool, v_pool [n_blocks, n_kv_heads, block_size, d_head] dtype, written
+ *   slot_mapping   [n_tokens] int32                           read
+ */
+int pa_cache_write(const void* key, const void* value, void* k_pool,
+                   void* v_pool, const int32_t* slot_mapping, int32_t n_tokens,
+                   int32_t n_kv_heads, int32_t d_head, int32_t block_size,
+                   int32_t n_blocks, int32_t dtype, void* stream);
+
+/*
+ * pa_decode -- one query token per sequence attends over all its cached
+ * positions, in one pass per (sequence, KV head).
+ *
+ * For query head h of sequence b, with kvh = h / gqa_group and n =
+ * context_lens[b] (the token written this step included):
+ *   s_t = scale * <q[b, h, :], K_t>            t = 0 .. n-1
+ *   out[b, h, :] = sum_t softmax(s)_t * V_t
+ * where K_t, V_t are row t of KV head kvh read through the block table.
+ * n == 0 gives a zero row.
+ *
+ *   out            [batch, n_kv_heads * gqa_group, d_head]   dtype, written
+ *   q              [batch, n_kv_heads * gqa_group, d_head]   dtype, read
+ *   k_pool, v_pool [n_blocks, n_kv_heads, block_size, d_head] dtype, read
+ *   block_table    [batch, max_blocks] int32                  read
+ *   context_lens   [batch] int32                              read
+ */
+int pa_decode(void* out, const void* q, const void* k_pool, const void* v_pool,
+              const int32_t* block_table, int32_t max_blocks,
+              const int32_t* context_lens, int32_t batch, int32_t n_kv_heads,
+              int32_t gqa_group, int32_t d_head, int32_t block_size,
+              int32_t n_blocks, float scale, int32_t dtype, void* stream);
+
+/*
+ * pa_decode_partitioned -- the same attention split along the context into
+ * partitions of partition_size positions, each reduced to softmax statistics
+ * that pa_reduce combines (log-sum-exp merge).  Partition p of sequence b
+ * covers positions [p * P, min((p + 1) * P, n)).  For each non-empty
+ * partition and query head, with s_t as in pa_decode:
+ *   max_logits[b, h, p] = m, a reference logit within 8 ln 2 below the
+ *                         partition's largest s_t (and not above it)
+ *   exp_sums[b, h, p]   = sum_t exp(s_t - m)
+ *   tmp_out[b, h, p, :] = sum_t exp(s_t - m) V_t / exp_sums[b, h, p]
+ * Entries of empty partitions (p * P >= n) are not written.
+ *
+ *   max_logits, exp_sums [batch, n_q_heads, max_partitions] float32, written
+ *   tmp_out   [batch, n_q_heads, max_partitions, d_head]     float32, written
+ *   max_partitions must be >= ceil(max_b context_lens[b] / partition_size);
+ *   sequences that need more get NaN outputs from pa_reduce.
+ *   Other arguments as in pa_decode.
+ */
+int pa_decode_partitioned(float* max_logits, float* exp_sums, float* tmp_out,
+                          int32_t partition_size, int32_t max_partitions,
+                          const void* q, const void* k_pool,
+                          const void* v_pool, const int32_t* block_table,
+                          int32_t max_blocks, const int32_t* context_lens,
+                          int32_t batch, int32_t n_kv_heads, int32_t gqa_group,
+                          int32_t d_head, int32_t block_size, int32_t n_blocks,
+                          float scale, int32_t dtype, void* stream);
+
+/*
+ * pa_reduce -- merge per-partition statistics into the attention output.
+ * With n_p = ceil(n / partition_size), M = max_{p<n_p} m_p and
+ * w_p = l_p * exp(m_p - M):
+ *   out[b, h, :] = sum_p w_p tmp_out[b, h, p, :] / sum_p w_p
+ * n == 0 gives a zero row.  Arrays as in pa_decode_partitioned; out as in
+ * pa_decode.
+ */
+int pa_reduce(void* out, const float* max_logits, const float* exp_sums,
+              const float* tmp_out, const int32_t* context_lens, int32_t batch,
+              int32_t n_q_heads, int32_t d_head, int32_t partition_size,
+              int32_t max_partitions, int32_t dtype, void* stream);
+
+/* Static text for a status code; never NULL. */
+const char* pa_strerror(int status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* PA_H_ */

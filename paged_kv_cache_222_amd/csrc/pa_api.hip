@@ -1,0 +1,218 @@
+// C ABI of libpa: argument checks, launch geometry, dispatch to the kernels.
+// Declarations and the full contract are in include/pa.h.
+#include <limits.h>
+
+#include "pa.h"
+#include "pa_launch.h"
+
+namespace {
+
+bool dtype_ok(int32_t dt) { return dt == PA_F32 || dt == PA_F16 || dt == PA_BF16; }
+int elem_bytes(int32_t dt) { return dt == PA_F32 ? 4 : 2; }
+bool dhead_ok(int32_t d) { return d == 64 || d == 128; }
+int block_shift_of(int32_t bs) {
+  switch (bs) {
+    case 8: return 3;
+    case 16: return 4;
+    case 32: return 5;
+    case 64: return 6;
+    default: return -1;
+  }
+}
+bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+bool aligned4(const void* p) { return ((uintptr_t)p & 3u) == 0; }
+
+int launch_status(hipError_t e) { return e == hipSuccess ? PA_OK : PA_ERR_HIP; }
+
+// Query heads per chunk: the whole group when it is at most 8, otherwise the
+// smallest even split into chunks of at most 8.
+void head_chunks(int32_t g, int* gc, int* nhc) {
+  *nhc = (g + 7) / 8;
+  *gc = (g + *nhc - 1) / *nhc;
+}
+
+// Shared checks of pa_decode and pa_decode_partitioned.
+int check_attention(const void* q, const void* k_pool, const void* v_pool,
+                    const int32_t* block_table, int32_t max_blocks,
+                    const int32_t* context_lens, int32_t batch, int32_t n_kv_heads,
+                    int32_t gqa_group, int32_t d_head, int32_t block_size,
+                    int32_t n_blocks, int32_t dtype) {
+  if (!q || !k_pool || !v_pool || !block_table || !context_lens) return PA_ERR_NULL;
+  if (!dtype_ok(dtype) || !dhead_ok(d_head) || block_shift_of(block_size) < 0)
+    return PA_ERR_UNSUPPORTED;
+  if (n_kv_heads < 1 || gqa_group < 1 || max_blocks < 1 || n_blocks < 1)
+    return PA_ERR_SHAPE;
+  if ((int64_t)n_kv_heads * gqa_group > INT_MAX / 4) return PA_ERR_SHAPE;
+  if ((int64_t)max_blocks * block_size > INT_MAX / 2) return PA_ERR_SHAPE;
+  if (!aligned16(q) || !aligned16(k_pool) || !aligned16(v_pool) || !aligned4(block_table) ||
+      !aligned4(context_lens))
+    return PA_ERR_ALIGN;
+  return PA_OK;
+}
+
+pa::AttnArgs attention_args(const void* q, const void* k_pool, const void* v_pool,
+                            const int32_t* block_table, int32_t max_blocks,
+                            const int32_t* context_lens, int32_t batch,
+                            int32_t n_kv_heads, int32_t gqa_group, int32_t block_size,
+                            int32_t n_blocks, float scale) {
+  pa::AttnArgs a{};
+  a.q = q;
+  a.k_pool = k_pool;
+  a.v_pool = v_pool;
+  a.block_table = block_table;
+  a.context_lens = context_lens;
+  a.max_blocks = max_blocks;
+  a.batch = batch;
+  a.n_kv_heads = n_kv_heads;
+  a.gqa_group = gqa_group;
+  int gc, nhc;
+  head_chunks(gqa_group, &gc, &nhc);
+  a.n_hchunks = nhc;
+  a.heads_per_chunk = gc;
+  a.block_shift = block_shift_of(block_size);
+  a.n_blocks = n_blocks;
+  a.scale_log2 = scale * 1.4426950408889634f;
+  return a;
+}
+
+hipError_t dispatch_attention(const pa::AttnArgs& a, int32_t dtype, int32_t d_head,
+                              unsigned grid, hipStream_t s) {
+  switch (dtype) {
+    case PA_F32: return pa::launch_attention_f32(a, d_head, a.heads_per_chunk, grid, s);
+    case PA_F16: return pa::launch_attention_f16(a, d_head, a.heads_per_chunk, grid, s);
+    case PA_BF16: return pa::launch_attention_bf16(a, d_head, a.heads_per_chunk, grid, s);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* pa_strerror(int status) {
+  switch (status) {
+    case PA_OK: return "ok";
+    case PA_ERR_NULL: return "a required pointer is NULL";
+    case PA_ERR_SHAPE: return "a size is negative, zero where it must be positive, or too large";
+    case PA_ERR_UNSUPPORTED: return "unsupported d_head, block_size or dtype";
+    case PA_ERR_WORKSPACE: return "max_partitions must be at least 1";
+    case PA_ERR_PARTITION: return "partition_size must be a positive multiple of block_size";
+    case PA_ERR_HIP: return "the HIP runtime reported an error at kernel launch";
+    case PA_ERR_ALIGN: return "an array pointer is not 16-byte aligned";
+    default: return "unknown status";
+  }
+}
+
+int pa_cache_write(const void* key, const void* value, void* k_pool, void* v_pool,
+                   const int32_t* slot_mapping, int32_t n_tokens, int32_t n_kv_heads,
+                   int32_t d_head, int32_t block_size, int32_t n_blocks, int32_t dtype,
+                   void* stream) {
+  if (n_tokens < 0) return PA_ERR_SHAPE;
+  if (n_tokens == 0) return PA_OK;
+  if (!key || !value || !k_pool || !v_pool || !slot_mapping) return PA_ERR_NULL;
+  if (!dtype_ok(dtype) || !dhead_ok(d_head) || block_shift_of(block_size) < 0)
+    return PA_ERR_UNSUPPORTED;
+  if (n_kv_heads < 1 || n_blocks < 1) return PA_ERR_SHAPE;
+  if ((int64_t)n_kv_heads * d_head * elem_bytes(dtype) > INT_MAX / 2) return PA_ERR_SHAPE;
+  if (!aligned16(key) || !aligned16(value) || !aligned16(k_pool) || !aligned16(v_pool) ||
+      !aligned4(slot_mapping))
+    return PA_ERR_ALIGN;
+  pa::CacheWriteArgs a{};
+  a.key = key;
+  a.value = value;
+  a.k_pool = k_pool;
+  a.v_pool = v_pool;
+  a.slot_mapping = slot_mapping;
+  a.n_tokens = n_tokens;
+  a.n_kv_heads = n_kv_heads;
+  a.row_bytes = d_head * elem_bytes(dtype);
+  a.block_shift = block_shift_of(block_size);
+  a.n_blocks = n_blocks;
+  (void)hipGetLastError();
+  return launch_status(pa::launch_cache_write(a, (hipStream_t)stream));
+}
+
+int pa_decode(void* out, const void* q, const void* k_pool, const void* v_pool,
+              const int32_t* block_table, int32_t max_blocks, const int32_t* context_lens,
+              int32_t batch, int32_t n_kv_heads, int32_t gqa_group, int32_t d_head,
+              int32_t block_size, int32_t n_blocks, float scale, int32_t dtype,
+              void* stream) {
+  if (batch < 0) return PA_ERR_SHAPE;
+  if (batch == 0) return PA_OK;
+  if (!out) return PA_ERR_NULL;
+  int st = check_attention(q, k_pool, v_pool, block_table, max_blocks, context_lens, batch,
+                           n_kv_heads, gqa_group, d_head, block_size, n_blocks, dtype);
+  if (st != PA_OK) return st;
+  if (!aligned16(out)) return PA_ERR_ALIGN;
+  pa::AttnArgs a = attention_args(q, k_pool, v_pool, block_table, max_blocks, context_lens,
+                                  batch, n_kv_heads, gqa_group, block_size, n_blocks, scale);
+  a.out = out;
+  a.partition_size = 0;
+  a.max_partitions = 0;
+  const int64_t grid = (int64_t)batch * n_kv_heads * a.n_hchunks;
+  if (grid > INT_MAX) return PA_ERR_SHAPE;
+  (void)hipGetLastError();
+  return launch_status(dispatch_attention(a, dtype, d_head, (unsigned)grid,
+                                          (hipStream_t)stream));
+}
+
+int pa_decode_partitioned(float* max_logits, float* exp_sums, float* tmp_out,
+                          int32_t partition_size, int32_t max_partitions, const void* q,
+                          const void* k_pool, const void* v_pool,
+                          const int32_t* block_table, int32_t max_blocks,
+                          const int32_t* context_lens, int32_t batch, int32_t n_kv_heads,
+                          int32_t gqa_group, int32_t d_head, int32_t block_size,
+                          int32_t n_blocks, float scale, int32_t dtype, void* stream) {
+  if (batch < 0) return PA_ERR_SHAPE;
+  if (batch == 0) return PA_OK;
+  if (!max_logits || !exp_sums || !tmp_out) return PA_ERR_NULL;
+  int st = check_attention(q, k_pool, v_pool, block_table, max_blocks, context_lens, batch,
+                           n_kv_heads, gqa_group, d_head, block_size, n_blocks, dtype);
+  if (st != PA_OK) return st;
+  if (partition_size <= 0 || partition_size % block_size != 0) return PA_ERR_PARTITION;
+  if (max_partitions < 1) return PA_ERR_WORKSPACE;
+  if (!aligned4(max_logits) || !aligned4(exp_sums) || !aligned16(tmp_out)) return PA_ERR_ALIGN;
+  pa::AttnArgs a = attention_args(q, k_pool, v_pool, block_table, max_blocks, context_lens,
+                                  batch, n_kv_heads, gqa_group, block_size, n_blocks, scale);
+  a.max_logits = max_logits;
+  a.exp_sums = exp_sums;
+  a.tmp_out = tmp_out;
+  a.partition_size = partition_size;
+  a.max_partitions = max_partitions;
+  const int64_t grid = (int64_t)max_partitions * batch * n_kv_heads * a.n_hchunks;
+  if (grid > INT_MAX) return PA_ERR_SHAPE;
+  (void)hipGetLastError();
+  return launch_status(dispatch_attention(a, dtype, d_head, (unsigned)grid,
+                                          (hipStream_t)stream));
+}
+
+int pa_reduce(void* out, const float* max_logits, const float* exp_sums,
+              const float* tmp_out, const int32_t* context_lens, int32_t batch,
+              int32_t n_q_heads, int32_t d_head, int32_t partition_size,
+              int32_t max_partitions, int32_t dtype, void* stream) {
+  if (batch < 0) return PA_ERR_SHAPE;
+  if (batch == 0) return PA_OK;
+  if (!out || !max_logits || !exp_sums || !tmp_out || !context_lens) return PA_ERR_NULL;
+  if (!dtype_ok(dtype) || !dhead_ok(d_head)) return PA_ERR_UNSUPPORTED;
+  if (n_q_heads < 1) return PA_ERR_SHAPE;
+  if (partition_size <= 0) return PA_ERR_PARTITION;
+  if (max_partitions < 1) return PA_ERR_WORKSPACE;
+  if ((int64_t)batch * n_q_heads > INT_MAX) return PA_ERR_SHAPE;
+  if (!aligned16(out) || !aligned4(max_logits) || !aligned4(exp_sums) ||
+      !aligned16(tmp_out) || !aligned4(context_lens))
+    return PA_ERR_ALIGN;
+  pa::ReduceArgs a{};
+  a.out = out;
+  a.max_logits = max_logits;
+  a.exp_sums = exp_sums;
+  a.tmp_out = tmp_out;
+  a.context_lens = context_lens;
+  a.batch = batch;
+  a.n_q_heads = n_q_heads;
+  a.partition_size = partition_size;
+  a.max_partitions = max_partitions;
+  (void)hipGetLastError();
+  return launch_status(pa::launch_reduce(a, dtype, d_head, (hipStream_t)stream));
+}
+
+}  // extern "C"

@@ -1,0 +1,11 @@
+// Attention kernels instantiated for the f16 element type.
+#include "pa_attention.h"
+
+namespace pa {
+
+hipError_t launch_attention_f16(const AttnArgs& a, int d_head, int heads_per_chunk,
+                                 unsigned grid, hipStream_t s) {
+  return launch_attention_dt<Dt::F16>(a, d_head, heads_per_chunk, grid, s);
+}
+
+}  // namespace pa

@@ -1,0 +1,74 @@
+// Host-side launch interface between the C ABI (pa_api.hip) and the kernel
+// translation units.  Not part of the public header.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace pa {
+
+// Arguments of the attention kernel.  partition_size == 0 selects the
+// single-pass mode (one work item covers a sequence's whole context and
+// writes `out`); otherwise each work item covers one partition and writes
+// max_logits / exp_sums / tmp_out.
+struct AttnArgs {
+  const void* q;
+  const void* k_pool;
+  const void* v_pool;
+  const int32_t* block_table;
+  const int32_t* context_lens;
+  void* out;
+  float* max_logits;
+  float* exp_sums;
+  float* tmp_out;
+  int32_t max_blocks;
+  int32_t batch;
+  int32_t n_kv_heads;
+  int32_t gqa_group;
+  int32_t n_hchunks;   // query-head chunks per KV head
+  int32_t heads_per_chunk;
+  int32_t block_shift; // log2(block_size)
+  int32_t n_blocks;
+  int32_t partition_size;
+  int32_t max_partitions;
+  float scale_log2;    // scale * log2(e)
+};
+
+struct ReduceArgs {
+  void* out;
+  const float* max_logits;
+  const float* exp_sums;
+  const float* tmp_out;
+  const int32_t* context_lens;
+  int32_t batch;
+  int32_t n_q_heads;
+  int32_t partition_size;
+  int32_t max_partitions;
+};
+
+struct CacheWriteArgs {
+  const void* key;
+  const void* value;
+  void* k_pool;
+  void* v_pool;
+  const int32_t* slot_mapping;
+  int32_t n_tokens;
+  int32_t n_kv_heads;
+  int32_t row_bytes;   // d_head * element size
+  int32_t block_shift;
+  int32_t n_blocks;
+};
+
+// Each returns a hipError_t from the launch.
+hipError_t launch_attention_f32(const AttnArgs& a, int d_head, int heads_per_chunk,
+                                unsigned grid, hipStream_t s);
+hipError_t launch_attention_f16(const AttnArgs& a, int d_head, int heads_per_chunk,
+                                unsigned grid, hipStream_t s);
+hipError_t launch_attention_bf16(const AttnArgs& a, int d_head, int heads_per_chunk,
+                                 unsigned grid, hipStream_t s);
+hipError_t launch_reduce(const ReduceArgs& a, int dtype, int d_head, hipStream_t s);
+hipError_t launch_cache_write(const CacheWriteArgs& a, hipStream_t s);
+
+constexpr int kAttnThreads = 256;  // four waves per work item
+
+}  // namespace pa

@@ -1,0 +1,74 @@
+// Merge of per-partition softmax statistics (log-sum-exp rule).
+//
+// Partition p of a sequence holds (m_p, l_p, o_p) with l_p = sum exp(s - m_p)
+// and o_p the normalised partial output.  Then l_p exp(m_p) is that
+// partition's softmax denominator, and attention over the whole context is
+// the mean of the o_p weighted by w_p = l_p exp(m_p - M), M = max_p m_p.
+// One wave per (sequence, query head); lanes own d_head/64 output elements.
+#include "pa_device.h"
+#include "pa_launch.h"
+
+namespace pa {
+
+template <Dt DT, int D>
+__global__ __launch_bounds__(kWave) void reduce_kernel(ReduceArgs a) {
+  constexpr int DPL = D / kWave;  // output elements per lane
+  const int lane = threadIdx.x;
+  const int bh = blockIdx.x;  // b * n_q_heads + h
+  const int b = bh / a.n_q_heads;
+  const int ctx = a.context_lens[b];
+  const int P = a.partition_size;
+  const int64_t orow = (int64_t)bh * D;
+  const int np = ctx > 0 ? (ctx + P - 1) / P : 0;
+  if (ctx < 0 || np > a.max_partitions || np == 0) {
+    const float v = np == 0 && ctx == 0 ? 0.0f : __builtin_nanf("");
+#pragma unroll
+    for (int k = 0; k < DPL; ++k) store_elem<DT>(a.out, orow + lane * DPL + k, v);
+    return;
+  }
+  const float* ml = a.max_logits + (int64_t)bh * a.max_partitions;
+  const float* es = a.exp_sums + (int64_t)bh * a.max_partitions;
+  const float* to = a.tmp_out + (int64_t)bh * a.max_partitions * D;
+
+  float M = -__builtin_huge_valf();
+  for (int p = lane; p < np; p += kWave) M = fmaxf(M, ml[p]);
+#pragma unroll
+  for (int s = 1; s < kWave; s <<= 1) M = fmaxf(M, shfl_xor_f(M, s));
+
+  float W = 0.0f;
+  float acc[DPL];
+#pragma unroll
+  for (int k = 0; k < DPL; ++k) acc[k] = 0.0f;
+  for (int p = 0; p < np; ++p) {
+    const float w = es[p] * exp2_fast((ml[p] - M) * kLog2e);
+    W += w;
+#pragma unroll
+    for (int k = 0; k < DPL; ++k)
+      acc[k] = __builtin_fmaf(w, to[(int64_t)p * D + lane * DPL + k], acc[k]);
+  }
+#pragma unroll
+  for (int k = 0; k < DPL; ++k) store_elem<DT>(a.out, orow + lane * DPL + k, acc[k] / W);
+}
+
+template <Dt DT>
+static hipError_t launch_reduce_dt(const ReduceArgs& a, int d_head, hipStream_t s) {
+  const unsigned grid = (unsigned)(a.batch * a.n_q_heads);
+  if (d_head == 64)
+    hipLaunchKernelGGL((reduce_kernel<DT, 64>), dim3(grid), dim3(kWave), 0, s, a);
+  else if (d_head == 128)
+    hipLaunchKernelGGL((reduce_kernel<DT, 128>), dim3(grid), dim3(kWave), 0, s, a);
+  else
+    return hipErrorInvalidValue;
+  return hipGetLastError();
+}
+
+hipError_t launch_reduce(const ReduceArgs& a, int dtype, int d_head, hipStream_t s) {
+  switch (dtype) {
+    case 0: return launch_reduce_dt<Dt::F32>(a, d_head, s);
+    case 1: return launch_reduce_dt<Dt::F16>(a, d_head, s);
+    case 2: return launch_reduce_dt<Dt::BF16>(a, d_head, s);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+}  // namespace pa

@@ -26,9 +26,10 @@ Storage dtypes: ``f32`` -> ``np.float32``, ``f16`` -> ``np.float16``,
 Pool slots that hold no token (the tail of each sequence's last block, unused
 blocks, and the new token's slot before it is written) are filled with NaN
 when ``poison=True`` so that a kernel which reads them without masking is
-caught.  Draw order from one ``numpy.random.Generator(PCG64DXSM(seed))``:
-lengths -> q -> K -> V -> new-token K -> new-token V -> placement (values
-before placement, so re-blocking a config keeps every token's values).
+caught.  Randomness: ``numpy.random.SeedSequence(seed).spawn(6)`` gives one
+``Generator(PCG64DXSM)`` each for the lengths, q, K, V, the new tokens' K then
+V, and the block placement, so re-blocking a config keeps every token's
+values.
 """
 
 from __future__ import annotations
@@ -253,6 +254,33 @@ class Workload:
         return tok * c.n_kv_heads * c.d_head * 2 * DTYPE_BYTES[c.dtype]
 
 
+_CHUNK = 1 << 22   # values per chunk of the K/V draws
+
+
+def _streams(seed: int):
+    """Independent generators for lengths, q, K, V, the new tokens' K/V and
+    block placement, spawned from one seed."""
+    kids = np.random.SeedSequence(seed).spawn(6)
+    return [np.random.Generator(np.random.PCG64DXSM(k)) for k in kids]
+
+
+def _fill_tokens(rng, pool, blk, off, std, dtype) -> None:
+    """Draw ``len(blk)`` tokens' values (float32 normals times ``std``,
+    rounded to ``dtype``) and store token i at ``pool[blk[i], :, off[i], :]``.
+    Works in chunks so no pool-sized temporaries are made."""
+    _, H, _, D = pool.shape
+    per = H * D
+    step = max(1, _CHUNK // per)
+    buf = np.empty(step * per, dtype=np.float32)
+    for s in range(0, len(blk), step):
+        n = min(step, len(blk) - s)
+        x = buf[:n * per]
+        rng.standard_normal(out=x, dtype=np.float32)
+        if std != 1.0:
+            x *= np.float32(std)
+        pool[blk[s:s + n], :, off[s:s + n], :] = encode(x, dtype).reshape(n, H, D)
+
+
 def _draw_lengths(cfg: Config, rng: np.random.Generator) -> np.ndarray:
     ctx = np.asarray(cfg.lengths(rng, cfg.batch), dtype=np.int64)
     return np.minimum(ctx, cfg.max_context)
@@ -263,8 +291,7 @@ def draw_lengths(cfg: Config | str, seed: int = 0) -> np.ndarray:
     drawing any values."""
     if isinstance(cfg, str):
         cfg = CONFIGS[cfg]
-    rng = np.random.Generator(np.random.PCG64DXSM(seed))
-    return _draw_lengths(cfg, rng).astype(np.int32)
+    return _draw_lengths(cfg, _streams(seed)[0]).astype(np.int32)
 
 
 def make_workload(cfg: Config | str, seed: int = 0, *, poison: bool = True,
@@ -283,30 +310,28 @@ def make_workload(cfg: Config | str, seed: int = 0, *, poison: bool = True,
         cfg = cfg.with_(block_size=block_size)
     if max_context is not None:
         cfg = cfg.with_(max_context=max_context)
-    rng = np.random.Generator(np.random.PCG64DXSM(seed))
+    rl, rq, rk, rv, rn, rp = _streams(seed)
     B, Hq, Hkv, D, BS = (cfg.batch, cfg.n_q_heads, cfg.n_kv_heads,
                           cfg.d_head, cfg.block_size)
     assert Hq % Hkv == 0
     assert cfg.prefix_len % BS == 0
 
     # 1. lengths
-    ctx = _draw_lengths(cfg, rng)
+    ctx = _draw_lengths(cfg, rl)
     assert (ctx >= 1).all()
     if cfg.prefix_len:
         assert (ctx > cfg.prefix_len).all()
 
-    # 2. values.  K/V are drawn per distinct cached token (prefix tokens once,
-    #    then each sequence's own tokens before its new one), in that order.
-    q = encode(rng.standard_normal((B, Hq, D), dtype=np.float32) * cfg.std,
+    # 2. values: q and the new tokens' K/V here; K and V of the distinct
+    #    cached tokens (prefix tokens once, then each sequence's own tokens
+    #    before its new one, in that order) are drawn in chunks straight into
+    #    the pool in step 4.
+    q = encode(rq.standard_normal((B, Hq, D), dtype=np.float32) * cfg.std,
                cfg.dtype)
     n_tok = cfg.prefix_len + int((ctx - 1 - cfg.prefix_len).sum())
-    k_tok = encode(rng.standard_normal((n_tok, Hkv, D), dtype=np.float32)
-                   * cfg.std, cfg.dtype)
-    v_tok = encode(rng.standard_normal((n_tok, Hkv, D), dtype=np.float32)
-                   * cfg.std, cfg.dtype)
-    key_new = encode(rng.standard_normal((B, Hkv, D), dtype=np.float32)
+    key_new = encode(rn.standard_normal((B, Hkv, D), dtype=np.float32)
                      * cfg.std, cfg.dtype)
-    value_new = encode(rng.standard_normal((B, Hkv, D), dtype=np.float32)
+    value_new = encode(rn.standard_normal((B, Hkv, D), dtype=np.float32)
                        * cfg.std, cfg.dtype)
 
     # 3. placement: logical blocks in canonical order (the shared prefix
@@ -318,7 +343,7 @@ def make_workload(cfg: Config | str, seed: int = 0, *, poison: bool = True,
     n_used = n_prefix_blocks + n_private
     n_blocks = cfg.pool_blocks if cfg.pool_blocks is not None else n_used
     assert n_blocks >= n_used, "pool too small"
-    phys = rng.permutation(n_blocks)[:n_used].astype(np.int64)
+    phys = rp.permutation(n_blocks)[:n_used].astype(np.int64)
     MB = cfg.max_blocks
     table = np.full((B, MB), -1, dtype=np.int32)
     cursor = n_prefix_blocks
@@ -345,9 +370,10 @@ def make_workload(cfg: Config | str, seed: int = 0, *, poison: bool = True,
         cur += n
     blk = table[tok_b, tok_t // BS].astype(np.int64)
     off = tok_t % BS
-    k_pool[blk, :, off, :] = k_tok
-    v_pool[blk, :, off, :] = v_tok
-    del k_tok, v_tok
+    del tok_b, tok_t
+    _fill_tokens(rk, k_pool, blk, off, cfg.std, cfg.dtype)
+    _fill_tokens(rv, v_pool, blk, off, cfg.std, cfg.dtype)
+    del blk, off
 
     pos = ctx - 1
     slot = table[np.arange(B), pos // BS].astype(np.int64) * BS + pos % BS

@@ -1,0 +1,177 @@
+"""The C ABI: the library loads, exports what include/pa.h declares, and
+rejects bad host-side arguments before touching the GPU (no compute calls
+here, so these run without a GPU)."""
+
+import ctypes
+import os
+import re
+import subprocess
+import sys
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "pa.h")
+
+PA_OK, PA_ERR_NULL, PA_ERR_SHAPE, PA_ERR_UNSUPPORTED = 0, -1, -2, -3
+PA_ERR_WORKSPACE, PA_ERR_PARTITION, PA_ERR_HIP, PA_ERR_ALIGN = -4, -5, -6, -7
+
+P = 0x100000        # a fake, 16-byte aligned device address (never touched)
+MIS = P + 8         # misaligned
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\s*\*?\s*(pa_\w+)\s*\(",
+                                 text, re.M)))
+
+
+def test_header_declares_the_entry_points():
+    assert declared_functions() == sorted(
+        ["pa_cache_write", "pa_decode", "pa_decode_partitioned", "pa_reduce",
+         "pa_strerror"])
+
+
+def test_library_exports_every_declared_symbol(lib):
+    from paged_kv_cache_222_amd import _binding
+    out = subprocess.run(["nm", "-D", "--defined-only",
+                          _binding.library_path()],
+                         capture_output=True, text=True, check=True).stdout
+    exported = {line.split()[-1] for line in out.splitlines() if line.strip()}
+    for name in declared_functions():
+        assert name in exported, name
+        assert hasattr(lib, name)
+
+
+def test_strerror_covers_every_status(lib):
+    seen = set()
+    for st in (PA_OK, PA_ERR_NULL, PA_ERR_SHAPE, PA_ERR_UNSUPPORTED,
+               PA_ERR_WORKSPACE, PA_ERR_PARTITION, PA_ERR_HIP, PA_ERR_ALIGN):
+        text = lib.pa_strerror(st).decode()
+        assert text and text != "unknown status"
+        seen.add(text)
+    assert len(seen) == 8
+    assert lib.pa_strerror(12345).decode() == "unknown status"
+
+
+def _cw(lib, **kw):
+    a = dict(key=P, value=P, k_pool=P, v_pool=P, slots=P, n=4, hkv=2, d=128,
+             bs=16, nb=8, dt=2)
+    a.update(kw)
+    return lib.pa_cache_write(a["key"], a["value"], a["k_pool"], a["v_pool"],
+                              a["slots"], a["n"], a["hkv"], a["d"], a["bs"],
+                              a["nb"], a["dt"], None)
+
+
+def test_cache_write_argument_checks(lib):
+    assert _cw(lib, n=0) == PA_OK                     # no-op, nothing launched
+    assert _cw(lib, n=-1) == PA_ERR_SHAPE
+    for k in ("key", "value", "k_pool", "v_pool", "slots"):
+        assert _cw(lib, **{k: None}) == PA_ERR_NULL, k
+    assert _cw(lib, d=96) == PA_ERR_UNSUPPORTED
+    assert _cw(lib, bs=12) == PA_ERR_UNSUPPORTED
+    assert _cw(lib, bs=128) == PA_ERR_UNSUPPORTED
+    assert _cw(lib, dt=3) == PA_ERR_UNSUPPORTED
+    assert _cw(lib, hkv=0) == PA_ERR_SHAPE
+    assert _cw(lib, nb=0) == PA_ERR_SHAPE
+    assert _cw(lib, key=MIS) == PA_ERR_ALIGN
+    assert _cw(lib, k_pool=MIS) == PA_ERR_ALIGN
+
+
+def _dec(lib, **kw):
+    a = dict(out=P, q=P, k=P, v=P, tbl=P, mb=16, ctx=P, B=4, hkv=2, G=4,
+             d=128, bs=16, nb=32, scale=0.1, dt=2)
+    a.update(kw)
+    return lib.pa_decode(a["out"], a["q"], a["k"], a["v"], a["tbl"], a["mb"],
+                         a["ctx"], a["B"], a["hkv"], a["G"], a["d"], a["bs"],
+                         a["nb"], a["scale"], a["dt"], None)
+
+
+def test_decode_argument_checks(lib):
+    assert _dec(lib, B=0) == PA_OK
+    assert _dec(lib, B=-2) == PA_ERR_SHAPE
+    for k in ("out", "q", "k", "v", "tbl", "ctx"):
+        assert _dec(lib, **{k: None}) == PA_ERR_NULL, k
+    assert _dec(lib, d=32) == PA_ERR_UNSUPPORTED
+    assert _dec(lib, bs=4) == PA_ERR_UNSUPPORTED
+    assert _dec(lib, dt=-1) == PA_ERR_UNSUPPORTED
+    assert _dec(lib, G=0) == PA_ERR_SHAPE
+    assert _dec(lib, hkv=0) == PA_ERR_SHAPE
+    assert _dec(lib, mb=0) == PA_ERR_SHAPE
+    assert _dec(lib, nb=0) == PA_ERR_SHAPE
+    assert _dec(lib, mb=2**30) == PA_ERR_SHAPE        # max_blocks*bs overflows
+    assert _dec(lib, q=MIS) == PA_ERR_ALIGN
+    assert _dec(lib, out=MIS) == PA_ERR_ALIGN
+    assert _dec(lib, tbl=P + 2) == PA_ERR_ALIGN
+
+
+def _part(lib, **kw):
+    a = dict(ml=P, es=P, to=P, psz=512, pmax=4, q=P, k=P, v=P, tbl=P, mb=64,
+             ctx=P, B=4, hkv=2, G=4, d=128, bs=16, nb=32, scale=0.1, dt=2)
+    a.update(kw)
+    return lib.pa_decode_partitioned(
+        a["ml"], a["es"], a["to"], a["psz"], a["pmax"], a["q"], a["k"],
+        a["v"], a["tbl"], a["mb"], a["ctx"], a["B"], a["hkv"], a["G"], a["d"],
+        a["bs"], a["nb"], a["scale"], a["dt"], None)
+
+
+def test_partitioned_argument_checks(lib):
+    assert _part(lib, B=0) == PA_OK
+    for k in ("ml", "es", "to", "q", "tbl"):
+        assert _part(lib, **{k: None}) == PA_ERR_NULL, k
+    assert _part(lib, psz=0) == PA_ERR_PARTITION
+    assert _part(lib, psz=24) == PA_ERR_PARTITION     # not a multiple of 16
+    assert _part(lib, psz=-16) == PA_ERR_PARTITION
+    assert _part(lib, pmax=0) == PA_ERR_WORKSPACE
+    assert _part(lib, d=256) == PA_ERR_UNSUPPORTED
+    assert _part(lib, to=MIS) == PA_ERR_ALIGN
+    assert _part(lib, pmax=2**20, B=2**12) == PA_ERR_SHAPE   # grid too large
+
+
+def _red(lib, **kw):
+    a = dict(out=P, ml=P, es=P, to=P, ctx=P, B=4, hq=8, d=128, psz=512,
+             pmax=4, dt=2)
+    a.update(kw)
+    return lib.pa_reduce(a["out"], a["ml"], a["es"], a["to"], a["ctx"],
+                         a["B"], a["hq"], a["d"], a["psz"], a["pmax"],
+                         a["dt"], None)
+
+
+def test_reduce_argument_checks(lib):
+    assert _red(lib, B=0) == PA_OK
+    for k in ("out", "ml", "es", "to", "ctx"):
+        assert _red(lib, **{k: None}) == PA_ERR_NULL, k
+    assert _red(lib, d=100) == PA_ERR_UNSUPPORTED
+    assert _red(lib, dt=9) == PA_ERR_UNSUPPORTED
+    assert _red(lib, hq=0) == PA_ERR_SHAPE
+    assert _red(lib, psz=0) == PA_ERR_PARTITION
+    assert _red(lib, pmax=0) == PA_ERR_WORKSPACE
+    assert _red(lib, out=MIS) == PA_ERR_ALIGN
+
+
+def test_binding_fails_loudly_without_library(tmp_path):
+    """With the library missing, the product path raises instead of
+    computing anything another way."""
+    env = dict(os.environ, PA_LIBRARY=str(tmp_path / "missing.so"))
+    code = ("import paged_kv_cache_222_amd as p\n"
+            "try:\n    p.load()\nexcept RuntimeError as e:\n"
+            "    print('RAISED', e)\n")
+    out = subprocess.run([sys.executable, "-c", code], cwd=ROOT, env=env,
+                         capture_output=True, text=True, check=True).stdout
+    assert "RAISED" in out and "missing.so" in out
+
+
+def test_binding_names_match_the_c_abi():
+    import paged_kv_cache_222_amd as p
+    for name in declared_functions():
+        assert callable(getattr(p, name)), name
+
+
+def test_product_code_never_imports_the_oracle():
+    pkg = os.path.join(ROOT, "paged_kv_cache_222_amd")
+    for dirpath, _, files in os.walk(pkg):
+        for f in files:
+            if f.endswith((".py", ".hip", ".h", ".cpp")):
+                text = open(os.path.join(dirpath, f)).read()
+                assert not re.search(r"^\s*(from|import)\s+oracle", text, re.M), f
+                assert "oracle/" not in text, f
