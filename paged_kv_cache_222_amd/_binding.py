@@ -34,11 +34,16 @@ def library_path() -> str:
 
 
 def load() -> ctypes.CDLL:
-    """Load libpa.so once; raise if it has not been built."""
+    """Load libpa.so once; raise if it has not been built.
+
+    torch is imported first so that libpa binds to the HIP runtime torch
+    ships (both carry the soname libamdhip64.so.7): torch's streams and
+    allocations are only valid in the runtime that made them."""
     global _lib
     with _lock:
         if _lib is not None:
             return _lib
+        import torch  # noqa: F401  (loads torch's HIP runtime first)
         path = library_path()
         if not os.path.exists(path):
             raise RuntimeError(

@@ -1,6 +1,8 @@
 // C ABI of libpa: argument checks, launch geometry, dispatch to the kernels.
 // Declarations and the full contract are in include/pa.h.
 #include <limits.h>
+#include <stdio.h>
+#include <stdlib.h>
 
 #include "pa.h"
 #include "pa_launch.h"
@@ -22,7 +24,14 @@ int block_shift_of(int32_t bs) {
 bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
 bool aligned4(const void* p) { return ((uintptr_t)p & 3u) == 0; }
 
-int launch_status(hipError_t e) { return e == hipSuccess ? PA_OK : PA_ERR_HIP; }
+// A failed launch returns PA_ERR_HIP; with PA_DEBUG set in the environment
+// the runtime's own message is also printed to stderr.
+int launch_status(hipError_t e) {
+  if (e == hipSuccess) return PA_OK;
+  if (getenv("PA_DEBUG"))
+    fprintf(stderr, "libpa: launch failed: %s (%d)\n", hipGetErrorString(e), (int)e);
+  return PA_ERR_HIP;
+}
 
 // Query heads per chunk: the whole group when it is at most 8, otherwise the
 // smallest even split into chunks of at most 8.

@@ -145,12 +145,13 @@ __global__ __launch_bounds__(kAttnThreads) void attention_kernel(AttnArgs a) {
   const int32_t* trow = a.block_table + (int64_t)b * a.max_blocks + first_blk;
 
   // ---- block-table window: lane j holds entry 64*w + j of this item.
-  int tw = -1, tbl_cur = 0, tbl_nxt = 0;
-  bool bad = false;
+  // tbl_nxt always holds window tw + 1 (loaded ahead); window 0 is first.
   auto raw_window = [&](int w) -> int {
     const int j = w * 64 + lane;
     return j < n_item_blocks ? trow[j] : 0;
   };
+  int tw = -1, tbl_cur = 0, tbl_nxt = raw_window(0);
+  bool bad = false;
   auto phys_of = [&](int pass) -> int {
     const int rel = ((t0 + pass * kPassTokens) >> a.block_shift) - first_blk;
     const int w = rel >> 6;

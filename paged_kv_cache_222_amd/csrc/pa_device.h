@@ -32,6 +32,11 @@ constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 
 __device__ __forceinline__ float as_f(uint32_t u) { return __builtin_bit_cast(float, u); }
+// Reinterpret a dword as two 16-bit lanes.  Takes the dword by value: with a
+// vector-element operand (v[j]) __builtin_bit_cast reads element 0 whatever j
+// is (seen with clang 22 for gfx950), so every caller passes a plain scalar.
+__device__ __forceinline__ bf16x2 as_bf16x2(uint32_t u) { return __builtin_bit_cast(bf16x2, u); }
+__device__ __forceinline__ f16x2 as_f16x2(uint32_t u) { return __builtin_bit_cast(f16x2, u); }
 __device__ __forceinline__ uint32_t as_u(float f) { return __builtin_bit_cast(uint32_t, f); }
 
 // 2^x on the transcendental unit (v_exp_f32).
@@ -65,8 +70,7 @@ template <>
 __device__ __forceinline__ float dot_chunk<Dt::BF16>(u32x4 k, u32x4 q, float acc) {
 #pragma unroll
   for (int j = 0; j < 4; ++j)
-    acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, k[j]),
-                                          __builtin_bit_cast(bf16x2, q[j]), acc, false);
+    acc = __builtin_amdgcn_fdot2_f32_bf16(as_bf16x2(k[j]), as_bf16x2(q[j]), acc, false);
   return acc;
 }
 
@@ -74,8 +78,7 @@ template <>
 __device__ __forceinline__ float dot_chunk<Dt::F16>(u32x4 k, u32x4 q, float acc) {
 #pragma unroll
   for (int j = 0; j < 4; ++j)
-    acc = __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2, k[j]),
-                                 __builtin_bit_cast(f16x2, q[j]), acc, false);
+    acc = __builtin_amdgcn_fdot2(as_f16x2(k[j]), as_f16x2(q[j]), acc, false);
   return acc;
 }
 
@@ -108,7 +111,7 @@ struct Unpack<Dt::F16> {
   __device__ __forceinline__ static void run(u32x4 v, float* f) {
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-      f16x2 h = __builtin_bit_cast(f16x2, v[j]);
+      const f16x2 h = as_f16x2(v[j]);
       f[2 * j] = (float)h[0];
       f[2 * j + 1] = (float)h[1];
     }

@@ -175,3 +175,16 @@ def test_product_code_never_imports_the_oracle():
                 text = open(os.path.join(dirpath, f)).read()
                 assert not re.search(r"^\s*(from|import)\s+oracle", text, re.M), f
                 assert "oracle/" not in text, f
+
+
+def test_one_hip_runtime_in_the_process():
+    """libpa must bind to the HIP runtime torch loads; two runtimes in one
+    process make torch's streams invalid for libpa's launches."""
+    code = ("import paged_kv_cache_222_amd as p\n"
+            "p.load()\n"
+            "import torch\n"
+            "maps = open('/proc/self/maps').read().splitlines()\n"
+            "print(len({l.split()[-1] for l in maps if 'libamdhip64' in l}))\n")
+    out = subprocess.run([sys.executable, "-c", code], cwd=ROOT,
+                         capture_output=True, text=True, check=True).stdout
+    assert out.strip() == "1"
