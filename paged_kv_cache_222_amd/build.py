@@ -24,9 +24,12 @@ LIB = os.path.join(PKG, "libpa.so")
 ARCH = "gfx950"
 
 # -packed-fp32-ops: never emit packed fp32 VALU ops (v_pk_{add,mul,fma}_f32).
+# -amdgpu-mfma-vgpr-form: MFMA accumulators in VGPRs, so the softmax rescale
+# of the accumulators needs no copies between register files.
 HIP_FLAGS = [
     f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC",
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    "-mllvm", "-amdgpu-mfma-vgpr-form",
     "-Wall", "-Wno-unused-function",
 ]
 
@@ -39,8 +42,8 @@ def hipcc() -> str:
     raise RuntimeError("hipcc not found (ROCm toolchain required)")
 
 
-def _compile(src: str, cc: str, extra) -> str:
-    obj = os.path.join(BUILD_DIR, os.path.basename(src)[:-4] + ".o")
+def _compile(src: str, cc: str, extra, build_dir: str) -> str:
+    obj = os.path.join(build_dir, os.path.basename(src)[:-4] + ".o")
     cmd = [cc, *HIP_FLAGS, *extra, f"-I{INCLUDE}", f"-I{CSRC}", "-c", src,
            "-o", obj]
     res = subprocess.run(cmd, capture_output=True, text=True)
@@ -50,27 +53,34 @@ def _compile(src: str, cc: str, extra) -> str:
     return obj
 
 
-def build(verbose: bool = False, extra_flags=()) -> str:
-    """Compile every HIP source and link libpa.so; returns its path."""
+def build(verbose: bool = False, extra_flags=(), out: str = LIB) -> str:
+    """Compile every HIP source and link libpa.so (or ``out``); returns its
+    path."""
     cc = hipcc()
-    os.makedirs(BUILD_DIR, exist_ok=True)
+    build_dir = BUILD_DIR if out == LIB else out + ".objs"
+    os.makedirs(build_dir, exist_ok=True)
     srcs = sorted(glob.glob(os.path.join(CSRC, "*.hip")))
     if not srcs:
         raise RuntimeError("no HIP sources found")
     jobs = min(len(srcs), max(1, min(8, os.cpu_count() or 1)))
     with concurrent.futures.ThreadPoolExecutor(jobs) as ex:
-        objs = list(ex.map(lambda s: _compile(s, cc, list(extra_flags)), srcs))
-    tmp = LIB + ".tmp"
+        objs = list(ex.map(lambda s: _compile(s, cc, list(extra_flags), build_dir),
+                           srcs))
+    tmp = out + ".tmp"
     cmd = [cc, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp, *objs]
     res = subprocess.run(cmd, capture_output=True, text=True)
     if res.returncode != 0:
         raise RuntimeError(f"link failed:\n{' '.join(cmd)}\n{res.stdout}\n"
                            f"{res.stderr}")
-    os.replace(tmp, LIB)
+    os.replace(tmp, out)
     if verbose:
-        print(f"built {LIB} from {len(srcs)} sources")
-    return LIB
+        print(f"built {out} from {len(srcs)} sources")
+    return out
 
 
 if __name__ == "__main__":
-    build(verbose=True, extra_flags=sys.argv[1:])
+    args = sys.argv[1:]
+    out = LIB
+    if args and args[0].startswith("--out="):
+        out = os.path.abspath(args.pop(0)[len("--out="):])
+    build(verbose=True, extra_flags=args, out=out)

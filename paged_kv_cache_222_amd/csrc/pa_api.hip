@@ -84,14 +84,56 @@ pa::AttnArgs attention_args(const void* q, const void* k_pool, const void* v_poo
   return a;
 }
 
-hipError_t dispatch_attention(const pa::AttnArgs& a, int32_t dtype, int32_t d_head,
-                              unsigned grid, hipStream_t s) {
-  switch (dtype) {
-    case PA_F32: return pa::launch_attention_f32(a, d_head, a.heads_per_chunk, grid, s);
-    case PA_F16: return pa::launch_attention_f16(a, d_head, a.heads_per_chunk, grid, s);
-    case PA_BF16: return pa::launch_attention_bf16(a, d_head, a.heads_per_chunk, grid, s);
-    default: return hipErrorInvalidValue;
+// Work groups of the matrix-core kernel that fit on the whole device, cached
+// per (device, dtype, d_head): an occupancy query per call would cost more
+// than a small decode step.
+int device_slots(int32_t dtype, int32_t d_head) {
+  static int cache[16][2][2];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 16) dev = 0;
+  int& c = cache[dev][dtype == PA_F16 ? 0 : 1][d_head == 64 ? 0 : 1];
+  if (c == 0) {
+    int cus = 0;
+    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+        cus < 1)
+      cus = 256;
+    c = cus * pa::attention_mfma_occupancy(dtype, d_head);
   }
+  return c;
+}
+
+// fp16/bf16 run on the matrix cores (query heads in chunks of 16); fp32 on
+// the vector ALUs (chunks of at most 8).  For a partitioned launch with a
+// batch the in-kernel plan can hold, the grid is sized to the device and
+// every work group loops over the non-empty items.
+hipError_t dispatch_attention(pa::AttnArgs a, int32_t dtype, int32_t d_head, int64_t rows,
+                              hipStream_t s, int* status) {
+  *status = PA_OK;
+  if (dtype == PA_F32) {
+    const int64_t grid = rows * a.n_kv_heads * a.n_hchunks;
+    if (grid > INT_MAX) {
+      *status = PA_ERR_SHAPE;
+      return hipSuccess;
+    }
+    return pa::launch_attention_f32(a, d_head, a.heads_per_chunk, (unsigned)grid, s);
+  }
+  a.n_hchunks = (a.gqa_group + pa::kMfmaHeads - 1) / pa::kMfmaHeads;
+  a.heads_per_chunk = pa::kMfmaHeads;
+  const int64_t cols = (int64_t)a.n_kv_heads * a.n_hchunks;
+  int64_t grid = rows * cols;
+  a.persistent = 0;
+  if (a.partition_size > 0 && a.batch <= pa::kPlanBatch) {
+    a.persistent = 1;
+    int64_t slots = device_slots(dtype, d_head);
+    if (slots >= cols) slots -= slots % cols;  // one KV head per work group
+    if (grid > slots) grid = slots;
+  }
+  if (grid > INT_MAX || cols > INT_MAX) {
+    *status = PA_ERR_SHAPE;
+    return hipSuccess;
+  }
+  return dtype == PA_F16 ? pa::launch_attention_mfma_f16(a, d_head, (unsigned)grid, s)
+                         : pa::launch_attention_mfma_bf16(a, d_head, (unsigned)grid, s);
 }
 
 }  // namespace
@@ -123,6 +165,8 @@ int pa_cache_write(const void* key, const void* value, void* k_pool, void* v_poo
     return PA_ERR_UNSUPPORTED;
   if (n_kv_heads < 1 || n_blocks < 1) return PA_ERR_SHAPE;
   if ((int64_t)n_kv_heads * d_head * elem_bytes(dtype) > INT_MAX / 2) return PA_ERR_SHAPE;
+  if ((int64_t)n_tokens * n_kv_heads * d_head * elem_bytes(dtype) / 16 / 256 >= INT_MAX)
+    return PA_ERR_SHAPE;  // launch grid
   if (!aligned16(key) || !aligned16(value) || !aligned16(k_pool) || !aligned16(v_pool) ||
       !aligned4(slot_mapping))
     return PA_ERR_ALIGN;
@@ -158,11 +202,10 @@ int pa_decode(void* out, const void* q, const void* k_pool, const void* v_pool,
   a.out = out;
   a.partition_size = 0;
   a.max_partitions = 0;
-  const int64_t grid = (int64_t)batch * n_kv_heads * a.n_hchunks;
-  if (grid > INT_MAX) return PA_ERR_SHAPE;
   (void)hipGetLastError();
-  return launch_status(dispatch_attention(a, dtype, d_head, (unsigned)grid,
-                                          (hipStream_t)stream));
+  int st2 = PA_OK;
+  const hipError_t e = dispatch_attention(a, dtype, d_head, batch, (hipStream_t)stream, &st2);
+  return st2 != PA_OK ? st2 : launch_status(e);
 }
 
 int pa_decode_partitioned(float* max_logits, float* exp_sums, float* tmp_out,
@@ -188,11 +231,12 @@ int pa_decode_partitioned(float* max_logits, float* exp_sums, float* tmp_out,
   a.tmp_out = tmp_out;
   a.partition_size = partition_size;
   a.max_partitions = max_partitions;
-  const int64_t grid = (int64_t)max_partitions * batch * n_kv_heads * a.n_hchunks;
-  if (grid > INT_MAX) return PA_ERR_SHAPE;
+  const int64_t rows = (int64_t)max_partitions * batch;
+  if (rows * n_kv_heads * ((gqa_group + 7) / 8) > INT_MAX) return PA_ERR_SHAPE;
   (void)hipGetLastError();
-  return launch_status(dispatch_attention(a, dtype, d_head, (unsigned)grid,
-                                          (hipStream_t)stream));
+  int st2 = PA_OK;
+  const hipError_t e = dispatch_attention(a, dtype, d_head, rows, (hipStream_t)stream, &st2);
+  return st2 != PA_OK ? st2 : launch_status(e);
 }
 
 int pa_reduce(void* out, const float* max_logits, const float* exp_sums,

@@ -86,7 +86,9 @@ __global__ __launch_bounds__(kAttnThreads) void attention_kernel(AttnArgs a) {
   int t0 = 0, t1 = ctx, p = 0;
   if (parts) {
     const int P = a.partition_size;
-    const int np = ctx > 0 ? (ctx + P - 1) / P : 0;
+    const int64_t np64 = ctx > 0 ? ((int64_t)ctx + P - 1) / P : 0;
+    if (np64 > a.max_partitions) return;  // pa_reduce reports NaN
+    const int np = (int)np64;
     // np > max_partitions (and ctx < 0) are reported as NaN by pa_reduce.
     if (np > a.max_partitions) return;
     // Rows are dispatched in order; row j holds partition np - PMAX + j, so
@@ -135,51 +137,43 @@ __global__ __launch_bounds__(kAttnThreads) void attention_kernel(AttnArgs a) {
   const int ntok = t1 - t0;
   const int npass = (ntok + kPassTokens - 1) / kPassTokens;
   const int my_n = npass > wave ? (npass - 1 - wave) / NW + 1 : 0;
-  const int first_blk = t0 >> a.block_shift;
-  const int n_item_blocks = ((t1 - 1) >> a.block_shift) - first_blk + 1;
   const int64_t tile_bytes = (int64_t)bs * RB;            // one (block, head)
   const int64_t blk_bytes = tile_bytes * a.n_kv_heads;    // one block
   const char* kbase = (const char*)a.k_pool + kvh * tile_bytes;
   const char* vbase = (const char*)a.v_pool + kvh * tile_bytes;
   const uint32_t lane_off = (uint32_t)(r * RB + c * 16);
-  const int32_t* trow = a.block_table + (int64_t)b * a.max_blocks + first_blk;
-
-  // ---- block-table window: lane j holds entry 64*w + j of this item.
-  // tbl_nxt always holds window tw + 1 (loaded ahead); window 0 is first.
-  auto raw_window = [&](int w) -> int {
-    const int j = w * 64 + lane;
-    return j < n_item_blocks ? trow[j] : 0;
-  };
-  int tw = -1, tbl_cur = 0, tbl_nxt = raw_window(0);
+  // The table row is read with scalar loads (constant address space): they
+  // are counted apart from the vector loads, so waiting for a block id never
+  // waits for K/V data in flight.
+  const __attribute__((address_space(4))) int32_t* trow =
+      (const __attribute__((address_space(4))) int32_t*)(a.block_table +
+                                                         (int64_t)b * a.max_blocks);
   bool bad = false;
-  auto phys_of = [&](int pass) -> int {
-    const int rel = ((t0 + pass * kPassTokens) >> a.block_shift) - first_blk;
-    const int w = rel >> 6;
-    if (w != tw) {
-      tbl_cur = (w == tw + 1) ? tbl_nxt : raw_window(w);
-      tw = w;
-      const int j = w * 64 + lane;
-      const bool inr = j < n_item_blocks;
-      const bool badl = inr && (tbl_cur < 0 || tbl_cur >= a.n_blocks);
-      if (__ballot(badl)) bad = true;
-      tbl_cur = (inr && !badl) ? tbl_cur : 0;
-      tbl_nxt = raw_window(w + 1);
-    }
-    return __builtin_amdgcn_readlane(tbl_cur, rel & 63);
-  };
 
-  auto load_pass = [&](int idx, u32x4 (&kc)[NC], u32x4 (&vc)[NC]) {
-    const int i2 = min(idx, my_n - 1);  // past the end: reload the last pass
-    const int pass = wave + i2 * NW;
-    const int phys = phys_of(pass);
-    const int off0 = (t0 + pass * kPassTokens) & (bs - 1);
-    const int64_t boff = (int64_t)phys * blk_bytes + (int64_t)off0 * RB;
-    const char* kp = kbase + boff;
-    const char* vp = vbase + boff;
+  // Pass idx of this wave (clamped: past the end it repeats the last pass,
+  // which keeps the number of loads in flight static).
+  auto pass_of = [&](int idx) { return wave + min(idx, my_n - 1) * NW; };
+  auto fetch_ids = [&](int idx0, int (&ph)[U]) {
 #pragma unroll
-    for (int i = 0; i < NC; ++i) {
-      kc[i] = *(const u32x4*)(kp + lane_off + i * 128);
-      vc[i] = *(const u32x4*)(vp + lane_off + i * 128);
+    for (int u = 0; u < U; ++u)
+      ph[u] = trow[(t0 + pass_of(idx0 + u) * kPassTokens) >> a.block_shift];
+  };
+  auto issue = [&](int idx0, const int (&ph)[U], u32x4 (&kc)[U][NC], u32x4 (&vc)[U][NC]) {
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int pass = pass_of(idx0 + u);
+      const bool ok = ph[u] >= 0 && ph[u] < a.n_blocks;
+      bad |= !ok;
+      const int64_t phys = ok ? ph[u] : 0;
+      const int off0 = (t0 + pass * kPassTokens) & (bs - 1);
+      const int64_t boff = phys * blk_bytes + (int64_t)off0 * RB;
+      const char* kp = kbase + boff;
+      const char* vp = vbase + boff;
+#pragma unroll
+      for (int i = 0; i < NC; ++i) {
+        kc[u][i] = *(const u32x4*)(kp + lane_off + i * 128);
+        vc[u][i] = *(const u32x4*)(vp + lane_off + i * 128);
+      }
     }
   };
 
@@ -193,9 +187,13 @@ __global__ __launch_bounds__(kAttnThreads) void attention_kernel(AttnArgs a) {
   }
   const float sl2 = a.scale_log2;
 
+  // One pass: logits of this lane's position for the GC heads, online
+  // softmax update, V accumulation.  All branches are wave-uniform; the
+  // partial last pass masks its invalid positions with selects.
   auto compute_pass = [&](int idx, const u32x4 (&kc)[NC], const u32x4 (&vc)[NC]) {
-    const int pass = wave + idx * NW;
-    const int tok = t0 + pass * kPassTokens + r;
+    const int tok0 = t0 + (wave + idx * NW) * kPassTokens;
+    const bool full = tok0 + kPassTokens <= t1;
+    const bool valid = tok0 + r < t1;
     float x[GC];
 #pragma unroll
     for (int g = 0; g < GC; ++g) {
@@ -203,48 +201,54 @@ __global__ __launch_bounds__(kAttnThreads) void attention_kernel(AttnArgs a) {
 #pragma unroll
       for (int i = 0; i < NC; ++i) acc = dot_chunk<DT>(kc[i], qv[g][i], acc);
       x[g] = sum8(acc) * sl2;
+      if (!full) x[g] = valid ? x[g] : -__builtin_huge_valf();
     }
-    if (tok < t1) {
-      bool need = false;
+    bool need = false;
 #pragma unroll
-      for (int g = 0; g < GC; ++g) need |= x[g] > m[g] + kTau;
-      if (need) {
-#pragma unroll
-        for (int g = 0; g < GC; ++g) {
-          const float mn = fmaxf(m[g], x[g]);
-          const float al = exp2_fast(m[g] - mn);
-          l[g] *= al;
-#pragma unroll
-          for (int e = 0; e < EPL; ++e) o[g][e] *= al;
-          m[g] = mn;
-        }
-      }
-      float vf[EPL];
-#pragma unroll
-      for (int i = 0; i < NC; ++i) Unpack<DT>::run(vc[i], vf + i * EPC);
+    for (int g = 0; g < GC; ++g) need |= x[g] > m[g] + kTau;
+    if (__ballot(need)) {
 #pragma unroll
       for (int g = 0; g < GC; ++g) {
-        const float pg = exp2_fast(x[g] - m[g]);
-        l[g] += pg;
+        const float mn = fmaxf(m[g], x[g]);
+        const float al = (m[g] == mn) ? 1.0f : exp2_fast(m[g] - mn);
+        l[g] *= al;
 #pragma unroll
-        for (int e = 0; e < EPL; ++e) o[g][e] = __builtin_fmaf(pg, vf[e], o[g][e]);
+        for (int e = 0; e < EPL; ++e) o[g][e] *= al;
+        m[g] = mn;
       }
+    }
+    float vf[EPL];
+#pragma unroll
+    for (int i = 0; i < NC; ++i) Unpack<DT>::run(vc[i], vf + i * EPC);
+    if (!full) {
+#pragma unroll
+      for (int e = 0; e < EPL; ++e) vf[e] = valid ? vf[e] : 0.0f;
+    }
+#pragma unroll
+    for (int g = 0; g < GC; ++g) {
+      float pg = exp2_fast(x[g] - m[g]);
+      if (!full) pg = valid ? pg : 0.0f;
+      l[g] += pg;
+#pragma unroll
+      for (int e = 0; e < EPL; ++e) o[g][e] = __builtin_fmaf(pg, vf[e], o[g][e]);
     }
   };
 
   if (my_n > 0) {
     u32x4 ka[U][NC], va[U][NC], kb[U][NC], vb[U][NC];
-#pragma unroll
-    for (int u = 0; u < U; ++u) load_pass(u, ka[u], va[u]);
+    int pa_[U], pb_[U];
+    fetch_ids(0, pa_);
+    issue(0, pa_, ka, va);
+    fetch_ids(U, pb_);
     for (int base = 0; base < my_n; base += 2 * U) {
-#pragma unroll
-      for (int u = 0; u < U; ++u) load_pass(base + U + u, kb[u], vb[u]);
+      issue(base + U, pb_, kb, vb);
+      fetch_ids(base + 2 * U, pa_);
 #pragma unroll
       for (int u = 0; u < U; ++u)
         if (base + u < my_n) compute_pass(base + u, ka[u], va[u]);
       if (base + U >= my_n) break;
-#pragma unroll
-      for (int u = 0; u < U; ++u) load_pass(base + 2 * U + u, ka[u], va[u]);
+      issue(base + 2 * U, pa_, ka, va);
+      fetch_ids(base + 3 * U, pb_);
 #pragma unroll
       for (int u = 0; u < U; ++u)
         if (base + U + u < my_n) compute_pass(base + U + u, kb[u], vb[u]);

@@ -1,0 +1,588 @@
+// Decode attention over a paged KV cache on the matrix cores (fp16/bf16).
+//
+// Computes, for every query head h of sequence b, softmax(scale * q K^T) V
+// over the sequence's cached positions read through its block table
+// ("Serving" section 23.2: decode reads the whole cached K/V of a sequence for
+// one query token; section 23.4: fixed-size blocks and a per-sequence table).
+// The G query heads that share a KV head (section 23.1) are one work item, so
+// each K/V byte is read from HBM once per step.
+//
+// Tiles of 16 consecutive positions.  For a tile:
+//   S = K Q^T       v_mfma_f32_16x16x32: A = K rows (lane l: position l%16,
+//                   16 bytes at dims 32j + 8(l/16)), loaded straight from HBM;
+//                   B = the queries (lane l: head l%16, zero past the group);
+//                   C = S (lane l: positions 4(l/16)+i, head l%16)
+//   P = exp2(S*scale*log2e - m), rounded to the storage type
+//   O += P V        v_mfma_f32_16x16x16: A = P, which is exactly the C layout
+//                   of S; B = V (lane l: positions 4(l/16)..+3 of dim l%16) —
+//                   V rows are copied HBM -> LDS with global_load_lds and read
+//                   back transposed with ds_read_b64_tr_b16.
+// The running maximum m is per head and shared by the four lanes holding that
+// head; it is raised only when a tile's maximum exceeds it by more than kTau
+// (log2 units), so exp2(S - m) <= 2^kTau.  The normaliser l sums the rounded
+// P, so the weights applied to V are exactly the ones summed.
+//
+// Work items are (sequence, KV head, chunk of <= 16 query heads[, partition])
+// and four waves share one item, taking its tiles round-robin; their states
+// are merged in LDS with the log-sum-exp rule at the end of the item.
+// Partitioned launches are persistent: each work group derives the list of
+// non-empty (sequence, partition) items from the context lengths, ordered
+// full partitions first and each sequence's final partial partition last,
+// and takes every gridDim.x-th item.  No work group is launched for an empty
+// partition.
+#pragma once
+
+#include <type_traits>
+
+#include "pa_device.h"
+#include "pa_launch.h"
+
+namespace pa {
+
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x8_t __attribute__((ext_vector_type(8)));
+typedef short s16x4_t __attribute__((ext_vector_type(4)));
+typedef _Float16 f16x4_t __attribute__((ext_vector_type(4)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
+
+constexpr int kMfmaTau = 8;          // lazy-rescale threshold, log2 units
+// Cache policy of the K/V copies: non-temporal ("nt"), since each byte is
+// read once per step.
+#ifndef PA_KV_NT
+#define PA_KV_NT 1
+#endif
+constexpr int kNonTemporal = PA_KV_NT ? 2 : 0;
+
+// s_waitcnt immediate that waits until at most n vector-memory operations of
+// this wave are outstanding (expcnt and lgkmcnt left unconstrained).
+constexpr int waitcnt_vm(int n) { return (n & 15) | (7 << 4) | (15 << 8) | (((n >> 4) & 3) << 14); }
+constexpr int kPlanMaxBatch = kPlanBatch;
+
+template <Dt DT>
+struct Mfma;
+
+template <>
+struct Mfma<Dt::BF16> {
+  __device__ __forceinline__ static f32x4_t qk(u32x4 a, u32x4 b, f32x4_t c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, a),
+                                                   __builtin_bit_cast(bf16x8_t, b), c, 0, 0, 0);
+  }
+  __device__ __forceinline__ static f32x4_t pv(u32x2_t a, u32x2_t b, f32x4_t c) {
+    return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(s16x4_t, a),
+                                                     __builtin_bit_cast(s16x4_t, b), c, 0, 0, 0);
+  }
+  // Round p to bf16 (nearest even); returns the bits, and the rounded value.
+  __device__ __forceinline__ static uint32_t round(float p, float& r) {
+    const __bf16 h = (__bf16)p;  // round to nearest even
+    const uint32_t bits = (uint32_t)__builtin_bit_cast(uint16_t, h);
+    r = as_f(bits << 16);
+    return bits;
+  }
+};
+
+template <>
+struct Mfma<Dt::F16> {
+  __device__ __forceinline__ static f32x4_t qk(u32x4 a, u32x4 b, f32x4_t c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8_t, a),
+                                                  __builtin_bit_cast(f16x8_t, b), c, 0, 0, 0);
+  }
+  __device__ __forceinline__ static f32x4_t pv(u32x2_t a, u32x2_t b, f32x4_t c) {
+    return __builtin_amdgcn_mfma_f32_16x16x16f16(__builtin_bit_cast(f16x4_t, a),
+                                                 __builtin_bit_cast(f16x4_t, b), c, 0, 0, 0);
+  }
+  __device__ __forceinline__ static uint32_t round(float p, float& r) {
+    const _Float16 h = (_Float16)p;
+    r = (float)h;
+    return (uint32_t)__builtin_bit_cast(uint16_t, h);
+  }
+};
+
+// LDS reads issued from inline assembly: the compiler would otherwise wait
+// for every outstanding HBM->LDS copy (vmcnt(0)) before any LDS read in a
+// loop, including copies into the other buffer.  The kernel orders the
+// copies with explicit vmcnt waits instead; lds_wait() then waits for these
+// reads and ties their results to the wait, so no use is scheduled earlier.
+template <int OFF>
+__device__ __forceinline__ u32x4 lds_read_b128(uint32_t addr) {
+  u32x4 r;
+  asm volatile("ds_read_b128 %0, %1 offset:%2" : "=v"(r) : "v"(addr), "i"(OFF));
+  return r;
+}
+template <int OFF>
+__device__ __forceinline__ u32x2_t lds_read_tr16(uint32_t addr) {
+  u32x2_t r;
+  asm volatile("ds_read_b64_tr_b16 %0, %1 offset:%2" : "=v"(r) : "v"(addr), "i"(OFF));
+  return r;
+}
+template <int N>
+__device__ __forceinline__ void lds_wait(u32x4 (&k)[N]) {
+  if constexpr (N == 2)
+    asm volatile("s_waitcnt lgkmcnt(0)" : "+v"(k[0]), "+v"(k[1])::"memory");
+  else
+    asm volatile("s_waitcnt lgkmcnt(0)" : "+v"(k[0]), "+v"(k[1]), "+v"(k[2]), "+v"(k[3])::"memory");
+}
+template <int N>
+__device__ __forceinline__ void lds_wait(u32x2_t (&v)[N]) {
+  if constexpr (N == 4)
+    asm volatile("s_waitcnt lgkmcnt(0)" : "+v"(v[0]), "+v"(v[1]), "+v"(v[2]), "+v"(v[3])::"memory");
+  else
+    asm volatile("s_waitcnt lgkmcnt(0)"
+                 : "+v"(v[0]), "+v"(v[1]), "+v"(v[2]), "+v"(v[3]), "+v"(v[4]), "+v"(v[5]),
+                   "+v"(v[6]), "+v"(v[7])::"memory");
+}
+template <int KQ, int ND, int TILE, int SLOT, int I>
+struct ReadTile {
+  __device__ __forceinline__ static void k(const uint32_t (&ka)[KQ], u32x4 (&kop)[KQ]) {
+    kop[I] = lds_read_b128<2 * SLOT * TILE>(ka[I]);
+    if constexpr (I + 1 < KQ) ReadTile<KQ, ND, TILE, SLOT, I + 1>::k(ka, kop);
+  }
+  __device__ __forceinline__ static void v(uint32_t va, u32x2_t (&vop)[ND]) {
+    vop[I] = lds_read_tr16<(2 * SLOT + 1) * TILE + 32 * I>(va);
+    if constexpr (I + 1 < ND) ReadTile<KQ, ND, TILE, SLOT, I + 1>::v(va, vop);
+  }
+};
+
+__device__ __forceinline__ int shfl_xor_i(int x, int m) {
+  return __builtin_amdgcn_ds_bpermute((__lane_id() ^ m) << 2, x);
+}
+__device__ __forceinline__ float shfl_from(float x, int src_lane) {
+  return as_f(__builtin_amdgcn_ds_bpermute(src_lane << 2, (int)as_u(x)));
+}
+
+// Inclusive prefix sum over the 64 lanes of a wave.
+__device__ __forceinline__ int wave_incl_scan(int x) {
+  const int lane = __lane_id();
+#pragma unroll
+  for (int d = 1; d < kWave; d <<= 1) {
+    const int y = __builtin_amdgcn_ds_bpermute((lane - d) << 2, x);
+    if (lane >= d) x += y;
+  }
+  return x;
+}
+
+// Largest i in [0, n) with pre[i] <= r, for a non-decreasing pre with
+// pre[0] <= r < pre[n].  pre lives in LDS; every lane computes the same i.
+__device__ __forceinline__ int plan_search(const int* pre, int n, int r) {
+  int lo = 0, hi = n;
+  while (hi - lo > 1) {
+    const int mid = (lo + hi) >> 1;
+    if (pre[mid] <= r)
+      lo = mid;
+    else
+      hi = mid;
+  }
+  return lo;
+}
+
+template <Dt DT, int D>
+#ifndef PA_MFMA_MIN_BLOCKS
+#define PA_MFMA_MIN_BLOCKS 2  // work groups per CU the register budget must allow
+#endif
+__global__ __launch_bounds__(kAttnThreads, PA_MFMA_MIN_BLOCKS) void attention_mfma_kernel(AttnArgs a) {
+  constexpr int RB = D * 2;                // bytes per (position, head) row
+  constexpr int NW = kAttnThreads / kWave;
+  constexpr int KQ = D / 32;               // QK MFMAs per tile
+  constexpr int ND = D / 16;               // PV MFMAs per tile
+  constexpr int TILE = 16 * RB;            // bytes of one 16-position tile
+  constexpr int NVI = TILE / 1024;         // 1 KiB copies per V tile
+  constexpr int CPR = RB / 16;             // 16-byte chunks per row
+  static_assert(NW * 16 * D * 4 <= NW * 4 * TILE, "merge buffer must fit the rings");
+
+  // Per wave, two slots (double buffer) of a K tile and a V tile; after the
+  // tiles of an item the same bytes hold the per-wave partial outputs.
+  __shared__ __attribute__((aligned(16))) char s_ring[NW * 4 * TILE];
+  __shared__ float s_m[NW][16];
+  __shared__ float s_l[NW][16];
+  __shared__ int s_bad[NW];
+  __shared__ int s_plan[2 * (kPlanMaxBatch + 1)];
+
+  const int lane = threadIdx.x & (kWave - 1);
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
+  const int l16 = lane & 15;
+  const int lg = lane >> 4;
+  const int bs = 1 << a.block_shift;
+  const int G = a.gqa_group;
+  const int Hq = a.n_kv_heads * G;
+  const int K = a.n_kv_heads * a.n_hchunks;
+  const bool parts = a.partition_size > 0;
+  const bool plan = parts && a.persistent;
+  const int P = a.partition_size;
+  const int64_t max_ctx = (int64_t)a.max_blocks << a.block_shift;
+
+  // ---- item list
+  int n_items, n_full = 0;
+  if (plan) {
+    // Thread t owns sequences 4t..4t+3.  full(b) = partitions before b's
+    // last one, tail(b) = 1 if b has any; exclusive prefix sums of both.
+    const int B = a.batch;
+    int fl[4], tl[4], fs = 0, ts = 0;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int b = threadIdx.x * 4 + j;
+      int np = 0;
+      if (b < B) {
+        const int c = a.context_lens[b];
+        // more than max_partitions is an error reported by pa_reduce; the
+        // cap keeps the item count in range
+        np = c > 0 ? (int)min(((int64_t)c + P - 1) / P, (int64_t)a.max_partitions + 1) : 0;
+      }
+      fl[j] = np > 0 ? np - 1 : 0;
+      tl[j] = np > 0 ? 1 : 0;
+      fs += fl[j];
+      ts += tl[j];
+    }
+    const int fi = wave_incl_scan(fs), ti = wave_incl_scan(ts);
+    if (lane == kWave - 1) {
+      s_m[wave][0] = __builtin_bit_cast(float, fi);
+      s_l[wave][0] = __builtin_bit_cast(float, ti);
+    }
+    __syncthreads();
+    int fo = 0, to = 0, ftot = 0, ttot = 0;
+#pragma unroll
+    for (int w = 0; w < NW; ++w) {
+      const int fw = __builtin_bit_cast(int, s_m[w][0]), tw = __builtin_bit_cast(int, s_l[w][0]);
+      if (w < wave) {
+        fo += fw;
+        to += tw;
+      }
+      ftot += fw;
+      ttot += tw;
+    }
+    int fx = fo + fi - fs, tx = to + ti - ts;  // exclusive offsets of b = 4t
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int b = threadIdx.x * 4 + j;
+      if (b < B) {
+        s_plan[b] = fx;
+        s_plan[kPlanMaxBatch + 1 + b] = tx;
+      }
+      fx += fl[j];
+      tx += tl[j];
+    }
+    if (threadIdx.x == 0) {
+      s_plan[B] = ftot;
+      s_plan[kPlanMaxBatch + 1 + B] = ttot;
+    }
+    __syncthreads();
+    n_full = ftot;
+    n_items = K * (ftot + ttot);
+  } else if (parts) {
+    n_items = K * a.batch * a.max_partitions;
+  } else {
+    n_items = K * a.batch;
+  }
+
+  const float sl2 = a.scale_log2;
+  const float qnan = __builtin_nanf("");
+  float* s_o = reinterpret_cast<float*>(s_ring);  // [NW][16][D] after the tiles
+
+  for (int item = blockIdx.x; item < n_items; item += gridDim.x) {
+    // ---- decode the item
+    const int kh = item % K;
+    const int rr = item / K;
+    const int kvh = kh / a.n_hchunks;
+    const int hc = kh - kvh * a.n_hchunks;
+    int b, p = 0;
+    if (plan) {
+      if (rr < n_full) {
+        b = plan_search(s_plan, a.batch, rr);
+        p = rr - s_plan[b];
+      } else {
+        b = plan_search(s_plan + kPlanMaxBatch + 1, a.batch, rr - n_full);
+        p = s_plan[b + 1] - s_plan[b];  // b's full partitions, then its tail
+      }
+    } else if (parts) {
+      const int j = rr / a.batch;
+      b = rr - j * a.batch;
+    } else {
+      b = rr;
+    }
+    b = __builtin_amdgcn_readfirstlane(b);
+    p = __builtin_amdgcn_readfirstlane(p);
+    const int ctx = a.context_lens[b];
+    const bool bad_ctx = ctx < 0 || (int64_t)ctx > max_ctx;
+    const int h0 = kvh * G + hc * 16;
+    const int gv = min(16, G - hc * 16);
+    int t0 = 0, t1 = ctx;
+    if (parts) {
+      const int64_t np = ctx > 0 ? ((int64_t)ctx + P - 1) / P : 0;
+      if (!plan) {
+        // one work group per (row, sequence): row j holds partition
+        // np - PMAX + j, so final partitions are dispatched last
+        if (np > a.max_partitions) continue;  // pa_reduce reports NaN
+        p = (int)np - a.max_partitions + rr / a.batch;
+        if (p < 0) continue;
+      } else if (np > a.max_partitions) {
+        continue;
+      }
+      if (bad_ctx) {
+        for (int idx = threadIdx.x; idx < gv * D; idx += kAttnThreads) {
+          const int g = idx / D, d = idx - g * D;
+          const int64_t prow = (int64_t)(b * Hq + h0 + g) * a.max_partitions + p;
+          a.tmp_out[prow * D + d] = qnan;
+          if (d == 0) {
+            a.max_logits[prow] = qnan;
+            a.exp_sums[prow] = qnan;
+          }
+        }
+        continue;
+      }
+      t0 = p * P;
+      t1 = min(t0 + P, ctx);
+    } else if (bad_ctx || ctx == 0) {
+      const float v = bad_ctx ? qnan : 0.0f;
+      for (int idx = threadIdx.x; idx < gv * D; idx += kAttnThreads) {
+        const int g = idx / D, d = idx - g * D;
+        store_elem<DT>(a.out, (int64_t)(b * Hq + h0 + g) * D + d, v);
+      }
+      continue;
+    }
+
+    // ---- queries of the chunk: B operand of S = K Q^T (zero past the group)
+    u32x4 qop[KQ];
+    {
+      const char* qrow = (const char*)a.q + (int64_t)(b * Hq + h0 + l16) * RB + lg * 16;
+#pragma unroll
+      for (int kk = 0; kk < KQ; ++kk)
+        qop[kk] = l16 < gv ? *(const u32x4*)(qrow + kk * 64) : u32x4{0u, 0u, 0u, 0u};
+    }
+
+    t0 = __builtin_amdgcn_readfirstlane(t0);
+    t1 = __builtin_amdgcn_readfirstlane(t1);
+    const int ntile = (t1 - t0 + 15) >> 4;
+    const int my_n = __builtin_amdgcn_readfirstlane(ntile > wave ? (ntile - 1 - wave) / NW + 1 : 0);
+    const int64_t head_bytes = (int64_t)bs * RB;        // one (block, KV head) tile
+    const int64_t blk_bytes = head_bytes * a.n_kv_heads;
+    const char* kbase = (const char*)a.k_pool + kvh * head_bytes;
+    const char* vbase = (const char*)a.v_pool + kvh * head_bytes;
+    const __attribute__((address_space(4))) int32_t* trow =
+        (const __attribute__((address_space(4))) int32_t*)(a.block_table +
+                                                           (int64_t)b * a.max_blocks);
+    char* my_ring = s_ring + wave * 4 * TILE;  // slot x: K at 2x*TILE, V at (2x+1)*TILE
+    bool bad = false;
+
+    // Byte offsets (in a KV head's view of a pool) of a tile's rows 0-7 and
+    // rows 8-15 (row r lives at base + r * RB).  With blocks of 16 or more
+    // positions a tile lies in one block and the two are equal; 8-position
+    // blocks give two blocks.
+    struct TileBase {
+      int64_t lo, hi;
+    };
+    auto tile_base = [&](int i) -> TileBase {
+      const int tok = __builtin_amdgcn_readfirstlane(t0 + (wave + i * NW) * 16);
+      // rows 8-15 past the end (tok + 8 >= t1) alias rows 0-7: in bounds,
+      // and masked out of the result
+      const int tok_hi = tok + 8 < t1 ? tok + 8 : tok;
+      const int bl0 = tok >> a.block_shift;
+      const int bl1 = tok_hi >> a.block_shift;
+      const int p0 = trow[bl0];
+      const int p1 = trow[bl1];
+      const bool ok0 = p0 >= 0 && p0 < a.n_blocks;
+      const bool ok1 = p1 >= 0 && p1 < a.n_blocks;
+      bad |= !(ok0 && ok1);
+      TileBase t;
+      t.lo = (ok0 ? (int64_t)p0 : 0) * blk_bytes + (int64_t)(tok & (bs - 1)) * RB;
+      t.hi = (ok1 ? (int64_t)p1 : 0) * blk_bytes + (int64_t)(tok_hi & (bs - 1)) * RB - 8 * RB;
+      return t;
+    };
+    // Copies HBM -> LDS, 1 KiB per instruction (16 bytes per lane).  The
+    // V tile is stored row-major (read back transposed); the K tile stores
+    // chunk c of row r at chunk c ^ (r % CPR) of that row, so the 16 lanes
+    // that read one column of 16 rows hit 16 different banks.
+    auto issue = [&](int i, int slot) {
+      const TileBase t = tile_base(i);
+      char* kd = my_ring + (2 * slot) * TILE;
+      char* vd = kd + TILE;
+#pragma unroll
+      for (int v = 0; v < NVI; ++v) {
+        const int sidx = v * 64 + lane;   // 16-byte slot in the tile
+        const int row = sidx / CPR;
+        const int64_t base = row >= 8 ? t.hi : t.lo;
+        const int kc = (sidx % CPR) ^ (row % CPR);
+        __builtin_amdgcn_global_load_lds(kbase + base + row * RB + kc * 16,
+                                         (__attribute__((address_space(3))) void*)(kd + v * 1024),
+                                         16, 0, kNonTemporal);
+        __builtin_amdgcn_global_load_lds(vbase + base + sidx * 16,
+                                         (__attribute__((address_space(3))) void*)(vd + v * 1024),
+                                         16, 0, kNonTemporal);
+      }
+    };
+
+    f32x4_t O[ND];
+#pragma unroll
+    for (int n = 0; n < ND; ++n) O[n] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    float m = -__builtin_huge_valf();  // running max (log2 units) of head l16
+    float lsum = 0.0f;                 // this lane's share of the normaliser
+    // LDS byte addresses of this lane's reads in slot 0 (slot 1 adds an
+    // immediate offset): K as the A operand (row l16, chunk 4kk + lg of the
+    // swizzled row), V transposed (rows 4lg..4lg+3, dims 4(l16%4).. of each
+    // 16-dim column block).
+    const uint32_t ring_lds = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) char*)my_ring;
+    uint32_t k_addr[KQ];
+#pragma unroll
+    for (int kk = 0; kk < KQ; ++kk)
+      k_addr[kk] = ring_lds + l16 * RB + (((kk * 4 + lg) ^ (l16 % CPR)) * 16);
+    const uint32_t v_addr = ring_lds + (lg * 4 + (l16 >> 2)) * RB + (l16 & 3) * 8;
+
+    auto compute = [&](int i, auto slot_tag) {
+      constexpr int SLOT = decltype(slot_tag)::value;
+      const int tok = __builtin_amdgcn_readfirstlane(t0 + (wave + i * NW) * 16);
+      const int nvalid = min(16, t1 - tok);
+      u32x4 kop[KQ];
+      ReadTile<KQ, ND, TILE, SLOT, 0>::k(k_addr, kop);
+      lds_wait(kop);
+      f32x4_t s = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int kk = 0; kk < KQ; ++kk) s = Mfma<DT>::qk(kop[kk], qop[kk], s);
+      float x[4];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) x[j] = s[j] * sl2;
+      if (nvalid < 16) {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) x[j] = (lg * 4 + j < nvalid) ? x[j] : -__builtin_huge_valf();
+      }
+      float bm = fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3]));
+      bm = fmaxf(bm, shfl_xor_f(bm, 16));
+      bm = fmaxf(bm, shfl_xor_f(bm, 32));
+      if (__ballot(bm > m + (float)kMfmaTau)) {
+        const float mn = fmaxf(m, bm);
+        const float al = (m == mn) ? 1.0f : exp2_fast(m - mn);
+        lsum *= al;
+        m = mn;
+        // O rows are heads 4*lg + j: fetch their factors from lanes 4*lg + j.
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const float aj = shfl_from(al, lg * 4 + j);
+#pragma unroll
+          for (int n = 0; n < ND; ++n) O[n][j] *= aj;
+        }
+      }
+      uint32_t pb[4];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        float r;
+        pb[j] = Mfma<DT>::round(exp2_fast(x[j] - m), r);
+        lsum += r;
+      }
+      const u32x2_t pa = u32x2_t{pb[0] | (pb[1] << 16), pb[2] | (pb[3] << 16)};
+      u32x2_t vop[ND];
+      ReadTile<KQ, ND, TILE, SLOT, 0>::v(v_addr, vop);
+      lds_wait(vop);
+      uint32_t vm0 = 0xFFFFFFFFu, vm1 = 0xFFFFFFFFu;
+      if (nvalid < 16) {
+        // zero V of positions past the end (they may hold NaN)
+        const int r0 = lg * 4;
+        vm0 = (r0 + 0 < nvalid ? 0x0000FFFFu : 0u) | (r0 + 1 < nvalid ? 0xFFFF0000u : 0u);
+        vm1 = (r0 + 2 < nvalid ? 0x0000FFFFu : 0u) | (r0 + 3 < nvalid ? 0xFFFF0000u : 0u);
+      }
+#pragma unroll
+      for (int n = 0; n < ND; ++n) {
+        u32x2_t vb = vop[n];
+        vb[0] &= vm0;
+        vb[1] &= vm1;
+        O[n] = Mfma<DT>::pv(pa, vb, O[n]);
+      }
+    };
+
+    if (my_n > 0) {
+      // Tile i + 1 is copied while tile i is computed.  Only the copies
+      // touch vmcnt in this loop, so "at most 2 * NVI outstanding" means
+      // tile i has landed.  The slots are compile-time offsets, which lets
+      // the compiler see that reading one slot does not wait for copies
+      // into the other.
+      issue(0, 0);
+      for (int i = 0; i < my_n; i += 2) {
+        if (i + 1 < my_n) {
+          issue(i + 1, 1);
+          __builtin_amdgcn_s_waitcnt(waitcnt_vm(2 * NVI));
+        } else {
+          __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
+        }
+        compute(i, std::integral_constant<int, 0>{});
+        if (i + 1 >= my_n) break;
+        if (i + 2 < my_n) {
+          issue(i + 2, 0);
+          __builtin_amdgcn_s_waitcnt(waitcnt_vm(2 * NVI));
+        } else {
+          __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
+        }
+        compute(i + 1, std::integral_constant<int, 1>{});
+      }
+    }
+
+    // ---- merge the waves
+    float lh = lsum + shfl_xor_f(lsum, 16);
+    lh += shfl_xor_f(lh, 32);
+    __syncthreads();  // every wave is done with its ring
+    if (lane < 16) {
+      s_m[wave][lane] = m;
+      s_l[wave][lane] = lh;
+    }
+    if (lane == 0) s_bad[wave] = bad ? 1 : 0;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int h = lg * 4 + j;
+      if (h < gv) {
+#pragma unroll
+        for (int n = 0; n < ND; ++n) s_o[(wave * 16 + h) * D + n * 16 + l16] = O[n][j];
+      }
+    }
+    __syncthreads();
+    bool anybad = false;
+#pragma unroll
+    for (int w = 0; w < NW; ++w) anybad |= s_bad[w] != 0;
+    for (int idx = threadIdx.x; idx < gv * D; idx += kAttnThreads) {
+      const int g = idx / D, d = idx - g * D;
+      float M = -__builtin_huge_valf();
+#pragma unroll
+      for (int w = 0; w < NW; ++w) M = fmaxf(M, s_m[w][g]);
+      float L = 0.0f, Ov = 0.0f;
+#pragma unroll
+      for (int w = 0; w < NW; ++w) {
+        const float mw = s_m[w][g];
+        const float aw = (mw == -__builtin_huge_valf()) ? 0.0f : exp2_fast(mw - M);
+        L += aw * s_l[w][g];
+        Ov += aw * s_o[(w * 16 + g) * D + d];
+      }
+      const int h = h0 + g;
+      if (parts) {
+        const int64_t prow = (int64_t)(b * Hq + h) * a.max_partitions + p;
+        a.tmp_out[prow * D + d] = anybad ? qnan : Ov / L;
+        if (d == 0) {
+          a.max_logits[prow] = anybad ? qnan : M * kLn2;
+          a.exp_sums[prow] = anybad ? qnan : L;
+        }
+      } else {
+        store_elem<DT>(a.out, (int64_t)(b * Hq + h) * D + d,
+                       anybad ? qnan : (L > 0.0f ? Ov / L : 0.0f));
+      }
+    }
+    __syncthreads();  // the merge buffer is the next item's rings
+  }
+}
+
+template <Dt DT>
+hipError_t launch_attention_mfma(const AttnArgs& a, int d_head, unsigned grid, hipStream_t s) {
+  if (d_head == 64)
+    hipLaunchKernelGGL((attention_mfma_kernel<DT, 64>), dim3(grid), dim3(kAttnThreads), 0, s, a);
+  else if (d_head == 128)
+    hipLaunchKernelGGL((attention_mfma_kernel<DT, 128>), dim3(grid), dim3(kAttnThreads), 0, s, a);
+  else
+    return hipErrorInvalidValue;
+  return hipGetLastError();
+}
+
+template <Dt DT>
+int attention_mfma_blocks_per_cu(int d_head) {
+  int n = 0;
+  if (d_head == 64)
+    (void)hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, attention_mfma_kernel<DT, 64>,
+                                                       kAttnThreads, 0);
+  else
+    (void)hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, attention_mfma_kernel<DT, 128>,
+                                                       kAttnThreads, 0);
+  return n > 0 ? n : 1;
+}
+
+}  // namespace pa

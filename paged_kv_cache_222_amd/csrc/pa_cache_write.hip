@@ -2,44 +2,43 @@
 //
 // The cache grows position by position into fixed-size blocks ("Serving"
 // section 23.4).  Flat slot s names block s >> block_shift, offset
-// s & (block_size - 1).  One wave per token copies its n_kv_heads rows of K and
-// of V with 16-byte loads and stores; a bit copy, no conversion.
+// s & (block_size - 1).  A bit copy, no conversion.
 #include "pa_device.h"
 #include "pa_launch.h"
 
 namespace pa {
 
-constexpr int kWriteWaves = 4;
+constexpr int kWriteThreads = 256;
 
-__global__ __launch_bounds__(kWave* kWriteWaves) void cache_write_kernel(CacheWriteArgs a) {
-  const int tok = blockIdx.x * kWriteWaves + (int)(threadIdx.x / kWave);
-  if (tok >= a.n_tokens) return;
-  const int lane = threadIdx.x & (kWave - 1);
+// One thread per 16-byte chunk of a (token, KV head) row: it copies that
+// chunk of K and of V.  Consecutive threads cover consecutive bytes of a
+// token's rows, so both the reads and the writes are whole lines.
+__global__ __launch_bounds__(kWriteThreads) void cache_write_kernel(CacheWriteArgs a) {
+  const int cpr = a.row_bytes >> 4;                 // chunks per row
+  const int64_t per_tok = (int64_t)a.n_kv_heads * cpr;
+  const int64_t gid = (int64_t)blockIdx.x * kWriteThreads + threadIdx.x;
+  if (gid >= per_tok * a.n_tokens) return;
+  const int tok = (int)(gid / per_tok);
+  const int rem = (int)(gid - (int64_t)tok * per_tok);
+  const int h = rem / cpr;
+  const int c = rem - h * cpr;
   const int slot = a.slot_mapping[tok];
   const int64_t n_slots = (int64_t)a.n_blocks << a.block_shift;
   if (slot < 0 || (int64_t)slot >= n_slots) return;
   const int64_t blk = slot >> a.block_shift;
   const int off = slot & ((1 << a.block_shift) - 1);
-  const int RB = a.row_bytes;
-  const int total = a.n_kv_heads * RB;
-  const char* ks = (const char*)a.key + (int64_t)tok * total;
-  const char* vs = (const char*)a.value + (int64_t)tok * total;
-  char* kd = (char*)a.k_pool;
-  char* vd = (char*)a.v_pool;
-  for (int x = lane * 16; x < total; x += kWave * 16) {
-    const int h = x / RB;
-    const int w = x - h * RB;
-    const int64_t dst = (((blk * a.n_kv_heads + h) << a.block_shift) + off) * RB + w;
-    const u32x4 kv = *(const u32x4*)(ks + x);
-    const u32x4 vv = *(const u32x4*)(vs + x);
-    *(u32x4*)(kd + dst) = kv;
-    *(u32x4*)(vd + dst) = vv;
-  }
+  const int64_t src = gid * 16;
+  const int64_t dst = (((blk * a.n_kv_heads + h) << a.block_shift) + off) * a.row_bytes + c * 16;
+  const u32x4 kv = *(const u32x4*)((const char*)a.key + src);
+  const u32x4 vv = *(const u32x4*)((const char*)a.value + src);
+  *(u32x4*)((char*)a.k_pool + dst) = kv;
+  *(u32x4*)((char*)a.v_pool + dst) = vv;
 }
 
 hipError_t launch_cache_write(const CacheWriteArgs& a, hipStream_t s) {
-  const unsigned grid = (unsigned)((a.n_tokens + kWriteWaves - 1) / kWriteWaves);
-  hipLaunchKernelGGL(cache_write_kernel, dim3(grid), dim3(kWave * kWriteWaves), 0, s, a);
+  const int64_t chunks = (int64_t)a.n_tokens * a.n_kv_heads * (a.row_bytes >> 4);
+  const unsigned grid = (unsigned)((chunks + kWriteThreads - 1) / kWriteThreads);
+  hipLaunchKernelGGL(cache_write_kernel, dim3(grid), dim3(kWriteThreads), 0, s, a);
   return hipGetLastError();
 }
 

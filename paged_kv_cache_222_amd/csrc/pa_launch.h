@@ -31,6 +31,7 @@ struct AttnArgs {
   int32_t n_blocks;
   int32_t partition_size;
   int32_t max_partitions;
+  int32_t persistent;  // partitioned launch sized to the GPU, items planned in-kernel
   float scale_log2;    // scale * log2(e)
 };
 
@@ -62,13 +63,17 @@ struct CacheWriteArgs {
 // Each returns a hipError_t from the launch.
 hipError_t launch_attention_f32(const AttnArgs& a, int d_head, int heads_per_chunk,
                                 unsigned grid, hipStream_t s);
-hipError_t launch_attention_f16(const AttnArgs& a, int d_head, int heads_per_chunk,
-                                unsigned grid, hipStream_t s);
-hipError_t launch_attention_bf16(const AttnArgs& a, int d_head, int heads_per_chunk,
-                                 unsigned grid, hipStream_t s);
+hipError_t launch_attention_mfma_f16(const AttnArgs& a, int d_head, unsigned grid,
+                                     hipStream_t s);
+hipError_t launch_attention_mfma_bf16(const AttnArgs& a, int d_head, unsigned grid,
+                                      hipStream_t s);
+// Work groups of the matrix-core attention kernel that fit on one CU.
+int attention_mfma_occupancy(int dtype, int d_head);
 hipError_t launch_reduce(const ReduceArgs& a, int dtype, int d_head, hipStream_t s);
 hipError_t launch_cache_write(const CacheWriteArgs& a, hipStream_t s);
 
 constexpr int kAttnThreads = 256;  // four waves per work item
+constexpr int kMfmaHeads = 16;     // query heads per work item on the matrix cores
+constexpr int kPlanBatch = 1024;   // largest batch the in-kernel partition plan handles
 
 }  // namespace pa

@@ -19,17 +19,19 @@ __global__ __launch_bounds__(kWave) void reduce_kernel(ReduceArgs a) {
   const int ctx = a.context_lens[b];
   const int P = a.partition_size;
   const int64_t orow = (int64_t)bh * D;
-  const int np = ctx > 0 ? (ctx + P - 1) / P : 0;
-  if (ctx < 0 || np > a.max_partitions || np == 0) {
-    const float v = np == 0 && ctx == 0 ? 0.0f : __builtin_nanf("");
+  const int64_t np64 = ctx > 0 ? ((int64_t)ctx + P - 1) / P : 0;
+  if (ctx < 0 || np64 > a.max_partitions || np64 == 0) {
+    const float v = (np64 == 0 && ctx == 0) ? 0.0f : __builtin_nanf("");
 #pragma unroll
     for (int k = 0; k < DPL; ++k) store_elem<DT>(a.out, orow + lane * DPL + k, v);
     return;
   }
+  const int np = (int)np64;
   const float* ml = a.max_logits + (int64_t)bh * a.max_partitions;
   const float* es = a.exp_sums + (int64_t)bh * a.max_partitions;
-  const float* to = a.tmp_out + (int64_t)bh * a.max_partitions * D;
+  const float* to = a.tmp_out + (int64_t)bh * a.max_partitions * D + lane * DPL;
 
+  // M over all partitions (lane p reads partitions p, p + 64, ...)
   float M = -__builtin_huge_valf();
   for (int p = lane; p < np; p += kWave) M = fmaxf(M, ml[p]);
 #pragma unroll
@@ -39,12 +41,35 @@ __global__ __launch_bounds__(kWave) void reduce_kernel(ReduceArgs a) {
   float acc[DPL];
 #pragma unroll
   for (int k = 0; k < DPL; ++k) acc[k] = 0.0f;
-  for (int p = 0; p < np; ++p) {
-    const float w = es[p] * exp2_fast((ml[p] - M) * kLog2e);
-    W += w;
+  for (int p0 = 0; p0 < np; p0 += kWave) {
+    // the weights of 64 partitions at once, one per lane
+    const int pl = p0 + lane;
+    const float w = pl < np ? es[pl] * exp2_fast((ml[pl] - M) * kLog2e) : 0.0f;
+    float ws = w;
 #pragma unroll
-    for (int k = 0; k < DPL; ++k)
-      acc[k] = __builtin_fmaf(w, to[(int64_t)p * D + lane * DPL + k], acc[k]);
+    for (int s = 1; s < kWave; s <<= 1) ws += shfl_xor_f(ws, s);
+    W += ws;
+    const int n = min(kWave, np - p0);
+    int j = 0;
+    for (; j + 4 <= n; j += 4) {
+      float wj[4], oj[4][DPL];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        wj[u] = as_f(__builtin_amdgcn_readlane((int)as_u(w), j + u));
+#pragma unroll
+        for (int k = 0; k < DPL; ++k) oj[u][k] = to[(int64_t)(p0 + j + u) * D + k];
+      }
+#pragma unroll
+      for (int u = 0; u < 4; ++u)
+#pragma unroll
+        for (int k = 0; k < DPL; ++k) acc[k] = __builtin_fmaf(wj[u], oj[u][k], acc[k]);
+    }
+    for (; j < n; ++j) {
+      const float wj = as_f(__builtin_amdgcn_readlane((int)as_u(w), j));
+#pragma unroll
+      for (int k = 0; k < DPL; ++k)
+        acc[k] = __builtin_fmaf(wj, to[(int64_t)(p0 + j) * D + k], acc[k]);
+    }
   }
 #pragma unroll
   for (int k = 0; k < DPL; ++k) store_elem<DT>(a.out, orow + lane * DPL + k, acc[k] / W);

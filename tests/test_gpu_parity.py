@@ -50,6 +50,7 @@ def run_decode(pa, d, name=""):
 
 
 def run_partitioned(pa, d, partition_size=None, max_partitions=None, name=""):
+    """pa_decode_partitioned + pa_reduce."""
     P = partition_size or d.partition_size
     pm = max_partitions or max(1, -(-int(d.w.context_lens.max()) // P))
     B, Hq, D = d.q.shape
@@ -120,15 +121,20 @@ def test_full_batch_step(pa, name, kw):
         c.gqa_group, c.block_size, c.dtype, c.partition_size,
         max_partitions=ws[0].shape[2], rows=sample)
     gm, gl, go = (from_dev(t).astype(np.float64) for t in ws)
+    # The softmax weights are rounded to the storage type before they
+    # multiply V (fp32 kept for fp32 data), and l sums the rounded weights:
+    # each weight is off by at most half an ulp (2^-9 bf16, 2^-12 fp16), so
+    # ln(l) moves by at most that much; the normalised partial output is a
+    # convex combination like the final one and gets the final tolerance.
+    lse_tol = {"bf16": 2.0 ** -8, "f16": 2.0 ** -11, "f32": 1e-5}[c.dtype]
     for b, h in sample:
         n_p = -(-int(w.context_lens[b]) // c.partition_size)
         lse_ref = m[b, h, :n_p] + np.log(l[b, h, :n_p])
         lse_gpu = gm[b, h, :n_p] + np.log(gl[b, h, :n_p])
-        assert np.max(np.abs(lse_gpu - lse_ref)) < 1e-4
+        assert np.max(np.abs(lse_gpu - lse_ref)) < lse_tol
         assert (gm[b, h, :n_p] <= m[b, h, :n_p] + 1e-5).all()
         assert (gm[b, h, :n_p] >= m[b, h, :n_p] - 8 * np.log(2) - 1e-5).all()
-        np.testing.assert_allclose(go[b, h, :n_p], o[b, h, :n_p], rtol=1e-4,
-                                   atol=1e-4)
+        assert np.max(np.abs(go[b, h, :n_p] - o[b, h, :n_p])) <= tol
 
 
 # ---------------------------------------------------------------------------
