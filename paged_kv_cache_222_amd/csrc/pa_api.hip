@@ -1,5 +1,6 @@
 // C ABI of libpa: argument checks, launch geometry, dispatch to the kernels.
 // Declarations and the full contract are in include/pa.h.
+#include <algorithm>
 #include <limits.h>
 #include <stdio.h>
 #include <stdlib.h>
@@ -122,11 +123,11 @@ hipError_t dispatch_attention(pa::AttnArgs a, int32_t dtype, int32_t d_head, int
   const int64_t cols = (int64_t)a.n_kv_heads * a.n_hchunks;
   int64_t grid = rows * cols;
   a.persistent = 0;
-  if (a.partition_size > 0 && a.batch <= pa::kPlanBatch) {
+  const int64_t slots = device_slots(dtype, d_head);
+  if (a.partition_size > 0 && a.batch <= pa::kPlanBatch && slots >= cols) {
+    // a whole number of work groups per column (KV head and head chunk)
     a.persistent = 1;
-    int64_t slots = device_slots(dtype, d_head);
-    if (slots >= cols) slots -= slots % cols;  // one KV head per work group
-    if (grid > slots) grid = slots;
+    grid = std::min(grid, slots - slots % cols);
   }
   if (grid > INT_MAX || cols > INT_MAX) {
     *status = PA_ERR_SHAPE;

@@ -195,7 +195,14 @@ __global__ __launch_bounds__(kAttnThreads, PA_MFMA_MIN_BLOCKS) void attention_mf
   __shared__ float s_m[NW][16];
   __shared__ float s_l[NW][16];
   __shared__ int s_bad[NW];
+  // Partitioned plan: exclusive prefix of the full partitions per sequence
+  // (and the total), then the sequences in the order their final partitions
+  // are dealt.  While it is built, the rings hold each sequence's sort key
+  // and rank.
   __shared__ int s_plan[2 * (kPlanMaxBatch + 1)];
+  int* s_key = reinterpret_cast<int*>(s_ring);
+  int* s_rank = s_key + kPlanMaxBatch;
+  static_assert(2 * kPlanMaxBatch * 4 <= NW * 4 * TILE, "plan keys must fit the rings");
 
   const int lane = threadIdx.x & (kWave - 1);
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
@@ -210,25 +217,36 @@ __global__ __launch_bounds__(kAttnThreads, PA_MFMA_MIN_BLOCKS) void attention_mf
   const int P = a.partition_size;
   const int64_t max_ctx = (int64_t)a.max_blocks << a.block_shift;
 
+  static_assert(kPlanMaxBatch == 4 * kAttnThreads && kPlanMaxBatch % 16 == 0,
+                "the plan gives each thread 4 sequences and reads keys 16 at a time");
   // ---- item list
   int n_items, n_full = 0;
   if (plan) {
     // Thread t owns sequences 4t..4t+3.  full(b) = partitions before b's
-    // last one, tail(b) = 1 if b has any; exclusive prefix sums of both.
+    // last one, tail(b) = 1 if b has any; the exclusive prefix sum of
+    // full(b), and the rank of b's final partition among all final
+    // partitions by decreasing length (ties by sequence).
     const int B = a.batch;
-    int fl[4], tl[4], fs = 0, ts = 0;
+    int fl[4], tl[4], key[4], fs = 0, ts = 0;
+    static_assert((int64_t)((1 << 20) - 1) * kPlanMaxBatch + kPlanMaxBatch < INT32_MAX, "plan keys fit 31 bits");
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       const int b = threadIdx.x * 4 + j;
-      int np = 0;
+      int np = 0, c = 0;
       if (b < B) {
-        const int c = a.context_lens[b];
+        c = a.context_lens[b];
         // more than max_partitions is an error reported by pa_reduce; the
         // cap keeps the item count in range
         np = c > 0 ? (int)min(((int64_t)c + P - 1) / P, (int64_t)a.max_partitions + 1) : 0;
       }
       fl[j] = np > 0 ? np - 1 : 0;
       tl[j] = np > 0 ? 1 : 0;
+      // final-partition length (capped at 2^20 - 1), ties broken by sequence:
+      // distinct keys, larger first; no final partition or padding: below all
+      const int64_t len = np > 0 ? min((int64_t)c - (int64_t)(np - 1) * P, (int64_t)(1 << 20) - 1) : -1;
+      key[j] = len >= 0 ? (int)(len * kPlanMaxBatch + (kPlanMaxBatch - 1 - b)) : -1 - (b >= B);
+      s_key[b] = key[j];
+      s_rank[b] = 0;
       fs += fl[j];
       ts += tl[j];
     }
@@ -238,35 +256,47 @@ __global__ __launch_bounds__(kAttnThreads, PA_MFMA_MIN_BLOCKS) void attention_mf
       s_l[wave][0] = __builtin_bit_cast(float, ti);
     }
     __syncthreads();
-    int fo = 0, to = 0, ftot = 0, ttot = 0;
+    int fo = 0, ftot = 0, ttot = 0;
 #pragma unroll
     for (int w = 0; w < NW; ++w) {
       const int fw = __builtin_bit_cast(int, s_m[w][0]), tw = __builtin_bit_cast(int, s_l[w][0]);
-      if (w < wave) {
-        fo += fw;
-        to += tw;
-      }
+      if (w < wave) fo += fw;
       ftot += fw;
       ttot += tw;
     }
-    int fx = fo + fi - fs, tx = to + ti - ts;  // exclusive offsets of b = 4t
+    // rank(b) = number of keys above b's; the B x B comparisons are split
+    // into (sequence, 16 keys) units over all threads and summed in LDS
+    // (integer sums: the result does not depend on the order).
+    {
+      const int ng = (B + 15) >> 4;
+      const int4* keys4 = reinterpret_cast<const int4*>(s_key);
+      for (int u = threadIdx.x; u < B * ng; u += kAttnThreads) {
+        const int b = u / ng, g = u - (u / ng) * ng;
+        const int kb = s_key[b];
+        int cnt = 0;
+#pragma unroll
+        for (int v = 0; v < 4; ++v) {
+          const int4 k4 = keys4[g * 4 + v];
+          cnt += (k4.x > kb) + (k4.y > kb) + (k4.z > kb) + (k4.w > kb);
+        }
+        atomicAdd(&s_rank[b], cnt);
+      }
+    }
+    __syncthreads();
+    int fx = fo + fi - fs;  // exclusive offset of b = 4t
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       const int b = threadIdx.x * 4 + j;
       if (b < B) {
         s_plan[b] = fx;
-        s_plan[kPlanMaxBatch + 1 + b] = tx;
+        if (tl[j]) s_plan[kPlanMaxBatch + 1 + s_rank[b]] = b;
       }
       fx += fl[j];
-      tx += tl[j];
     }
-    if (threadIdx.x == 0) {
-      s_plan[B] = ftot;
-      s_plan[kPlanMaxBatch + 1 + B] = ttot;
-    }
+    if (threadIdx.x == 0) s_plan[B] = ftot;
     __syncthreads();
     n_full = ftot;
-    n_items = K * (ftot + ttot);
+    n_items = ftot + ttot;  // per column
   } else if (parts) {
     n_items = K * a.batch * a.max_partitions;
   } else {
@@ -277,10 +307,27 @@ __global__ __launch_bounds__(kAttnThreads, PA_MFMA_MIN_BLOCKS) void attention_mf
   const float qnan = __builtin_nanf("");
   float* s_o = reinterpret_cast<float*>(s_ring);  // [NW][16][D] after the tiles
 
-  for (int item = blockIdx.x; item < n_items; item += gridDim.x) {
+  // Persistent launches: the grid is W work groups per column (a KV head and
+  // head chunk), and work group j of a column takes its column's items
+  // j, 2W-1-j, 2W+j, 4W-1-j, ... of the plan (full partitions, then final
+  // partitions longest first): dealt back and forth, so the work groups of
+  // a column end with nearly equal loads.  Other launches take every
+  // gridDim.x-th (item, column) pair.
+  const int W = plan ? (int)gridDim.x / K : 0;
+  const int jw = plan ? (int)blockIdx.x / K : 0;
+  for (int it = 0;; ++it) {
     // ---- decode the item
-    const int kh = item % K;
-    const int rr = item / K;
+    int kh, rr;
+    if (plan) {
+      kh = blockIdx.x % K;
+      rr = it * W + ((it & 1) ? W - 1 - jw : jw);
+      if (rr >= n_items) break;
+    } else {
+      const int item = blockIdx.x + it * gridDim.x;
+      if (item >= n_items) break;
+      kh = item % K;
+      rr = item / K;
+    }
     const int kvh = kh / a.n_hchunks;
     const int hc = kh - kvh * a.n_hchunks;
     int b, p = 0;
@@ -289,7 +336,7 @@ __global__ __launch_bounds__(kAttnThreads, PA_MFMA_MIN_BLOCKS) void attention_mf
         b = plan_search(s_plan, a.batch, rr);
         p = rr - s_plan[b];
       } else {
-        b = plan_search(s_plan + kPlanMaxBatch + 1, a.batch, rr - n_full);
+        b = s_plan[kPlanMaxBatch + 1 + rr - n_full];
         p = s_plan[b + 1] - s_plan[b];  // b's full partitions, then its tail
       }
     } else if (parts) {
@@ -300,7 +347,8 @@ __global__ __launch_bounds__(kAttnThreads, PA_MFMA_MIN_BLOCKS) void attention_mf
     }
     b = __builtin_amdgcn_readfirstlane(b);
     p = __builtin_amdgcn_readfirstlane(p);
-    const int ctx = a.context_lens[b];
+    // a scalar read (the table and lengths are not written by this kernel)
+    const int ctx = ((const __attribute__((address_space(4))) int32_t*)a.context_lens)[b];
     const bool bad_ctx = ctx < 0 || (int64_t)ctx > max_ctx;
     const int h0 = kvh * G + hc * 16;
     const int gv = min(16, G - hc * 16);
@@ -486,9 +534,10 @@ __global__ __launch_bounds__(kAttnThreads, PA_MFMA_MIN_BLOCKS) void attention_mf
     };
 
     if (my_n > 0) {
-      // Tile i + 1 is copied while tile i is computed.  Only the copies
-      // touch vmcnt in this loop, so "at most 2 * NVI outstanding" means
-      // tile i has landed.  The slots are compile-time offsets, which lets
+      // Tile i + 1 is copied while tile i is computed.  Loads (and these
+      // copies) complete in issue order, so "at most 2 * NVI outstanding"
+      // right after tile i + 1's copies are issued means tile i, and
+      // anything issued before it, has landed.  The slots are compile-time offsets, which lets
       // the compiler see that reading one slot does not wait for copies
       // into the other.
       issue(0, 0);
