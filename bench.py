@@ -53,6 +53,11 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
                     help="budget of the CPU oracle sample")
+    ap.add_argument("--op", choices=["decode", "copy-blocks"], default="decode",
+                    help="decode: the decode step (default); copy-blocks: "
+                         "the copy-on-write block copy on the LLaMA-3-8B pool")
+    ap.add_argument("--pairs", type=int, default=4096,
+                    help="copy-blocks: block pairs per call")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only run a plain device-to-device copy of MIB MiB "
                          "five times and exit: the known-size kernel that "
@@ -125,6 +130,86 @@ def copy_calibration(mib):
         "per launch)")
 
 
+def bench_copy_blocks(args, torch, pa, wl):
+    """pa_copy_blocks on the LLaMA-3-8B pool plus args.pairs free blocks:
+    each call copies args.pairs used blocks (K and V, all KV heads) into the
+    free ones; three pair lists rotate so that no call finds its sources in
+    the last-level cache."""
+    w = wl.make_workload("llama3-8b", seed=args.seed)
+    c = w.cfg
+    n_used = w.k_pool.shape[0]
+    n_total = n_used + args.pairs
+    tdt = {"f16": torch.float16, "bf16": torch.bfloat16}[c.dtype]
+    shape = (n_total,) + w.k_pool.shape[1:]
+    k = torch.empty(shape, dtype=tdt, device="cuda")
+    v = torch.empty(shape, dtype=tdt, device="cuda")
+    k[:n_used].copy_(torch.from_numpy(w.k_pool.view(np.int16)).view(tdt))
+    v[:n_used].copy_(torch.from_numpy(w.v_pool.view(np.int16)).view(tdt))
+    lists = []
+    for i in range(3):
+        rng = np.random.default_rng(1000 + i)
+        src = rng.integers(0, n_used, args.pairs)
+        dst = n_used + rng.permutation(args.pairs)
+        lists.append(torch.from_numpy(np.ascontiguousarray(
+            np.stack([src, dst], axis=1).astype(np.int32))).cuda())
+    block_bytes = int(np.prod(shape[1:])) * 2
+    moved = 2 * 2 * block_bytes * args.pairs        # K and V, read + write
+    stream = torch.cuda.current_stream()
+    for i in range(args.warmup):
+        pa.pa_copy_blocks(k, v, lists[i % 3])
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        pa.pa_copy_blocks(k, v, lists[i % 3])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ev = [(torch.cuda.Event(enable_timing=True),
+           torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+    for i in range(args.steps):
+        ev[i][0].record(stream)
+        pa.pa_copy_blocks(k, v, lists[i % 3])
+        ev[i][1].record(stream)
+    torch.cuda.synchronize()
+    us = float(np.mean([a.elapsed_time(b) for a, b in ev])) * 1e3
+    ms = wall / args.steps * 1e3
+    rec = {
+        "metric": "copy-on-write block copy GB/s (bytes read + written)",
+        "value": round(moved / (ms * 1e-3) / 1e9, 2), "unit": "GB/s",
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": round(ms, 5), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": c.dtype,
+        "data": "synthetic",
+        "config": {"workload": f"pa_copy_blocks: {args.pairs} blocks of the "
+                               f"llama3-8b pool ({n_used} blocks in use, "
+                               f"{block_bytes} B per block per pool) into "
+                               "free blocks", "pairs": args.pairs,
+                   "block_bytes": block_bytes, "seed": args.seed},
+        "roofline": {"kernel": "copy_blocks_kernel (pa_copy_blocks)",
+                     "bound": "hbm", "achieved": round(moved / (us * 1e-6) / 1e9, 1),
+                     "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(moved / (us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
+                     "traffic": None, "algorithmic_bytes_per_launch": moved,
+                     "avg_launch_us": round(us, 3)},
+    }
+    if not args.no_cpu_baseline:
+        import oracle
+        kh = w.k_pool[:min(n_used, 2048)]
+        vh = w.v_pool[:min(n_used, 2048)]
+        pairs = np.stack([np.arange(0, 512), np.arange(512, 1024)], axis=1)
+        t0 = time.perf_counter()
+        reps = 0
+        while time.perf_counter() - t0 < min(args.cpu_seconds, 10.0):
+            oracle.oracle_copy_blocks(kh, vh, pairs)
+            reps += 1
+        dt = time.perf_counter() - t0
+        rec["cpu_baseline"] = {
+            "value": round(reps * 2 * 2 * block_bytes * len(pairs) / dt / 1e9, 4),
+            "unit": "GB/s", "cores": 1, "kind": "oracle",
+            "sample": f"{reps} calls of 512 pairs on a 2048-block slice of the "
+                      f"pool (numpy copies of whole pools included), {dt:.1f} s"}
+    print(json.dumps(rec), flush=True)
+
+
 def cpu_baseline(w, budget_s):
     """The fp64 oracle on the host cores, over the first sequences of the
     batch (all query heads) until the time budget is spent."""
@@ -177,6 +262,9 @@ def main():
         copy_calibration(args.copy_calibration)
         return
     pa.load()
+    if args.op == "copy-blocks":
+        bench_copy_blocks(args, torch, pa, wl)
+        return
     kw = {}
     if args.block_size:
         kw["block_size"] = args.block_size

@@ -90,6 +90,29 @@ int pa_cache_write(const void* key, const void* value, void* k_pool,
                    int32_t n_blocks, int32_t dtype, void* stream);
 
 /*
+ * pa_copy_blocks -- copy whole physical blocks within both pools, so that a
+ * block shared by several sequences can be duplicated before one of them
+ * writes into it (copy-on-write sharing of the paged cache: the "Paged
+ * Attention" summary on the inference-serving tag page; sequences sharing a
+ * prefix share its blocks, "Serving" section 23.4).
+ *
+ * For i < n_pairs with s = block_pairs[2i], d = block_pairs[2i + 1]:
+ *   k_pool[d, :, :, :] = k_pool[s, :, :, :]   and   v_pool[d] = v_pool[s]
+ * A bit copy.  Every pair reads the pools as they were before the call:
+ * destinations must be distinct and must not be the source of any pair
+ * (otherwise the result is unspecified).  A pair naming a block outside
+ * [0, n_blocks) is skipped.  The caller updates its block tables.
+ *
+ *   k_pool, v_pool [n_blocks, n_kv_heads, block_size, d_head] dtype, read and
+ *                  written
+ *   block_pairs    [n_pairs, 2] int32 (source, destination)       read
+ */
+int pa_copy_blocks(void* k_pool, void* v_pool, const int32_t* block_pairs,
+                   int32_t n_pairs, int32_t n_kv_heads, int32_t d_head,
+                   int32_t block_size, int32_t n_blocks, int32_t dtype,
+                   void* stream);
+
+/*
  * pa_decode -- one query token per sequence attends over all its cached
  * positions, in one pass per (sequence, KV head).
  *

@@ -8,6 +8,7 @@ the HIP library or its Python binding.
 from .paged_attention import (  # noqa: F401
     kv_cache_bytes,
     oracle_cache_write,
+    oracle_copy_blocks,
     oracle_decode,
     oracle_decode_row,
     oracle_merge,

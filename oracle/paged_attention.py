@@ -120,6 +120,34 @@ def oracle_cache_write(k_pool: np.ndarray, v_pool: np.ndarray,
 
 
 # ---------------------------------------------------------------------------
+# Block copy (copy-on-write)
+# ---------------------------------------------------------------------------
+
+
+def oracle_copy_blocks(k_pool: np.ndarray, v_pool: np.ndarray,
+                       block_pairs: np.ndarray):
+    """Whole physical blocks duplicated in both pools, as a bit copy.
+
+    Sequences that share a prefix share its blocks ("Serving", §23.4); with
+    copy-on-write sharing (named in the "Paged Attention" summary on the
+    inference-serving tag page) a shared block is duplicated before one
+    sharer writes into it.  For each row ``(s, d)`` of ``block_pairs``, block
+    ``d`` of each pool becomes a copy of block ``s`` as it was before the
+    call (every KV head, position and dimension); a row naming a block
+    outside the pool is skipped.  Returns new pools; the inputs are not
+    modified."""
+    k_out = k_pool.copy()
+    v_out = v_pool.copy()
+    n_blocks = k_pool.shape[0]
+    for s, d in np.asarray(block_pairs).reshape(-1, 2).tolist():
+        if not (0 <= s < n_blocks and 0 <= d < n_blocks):
+            continue
+        k_out[d] = k_pool[s]
+        v_out[d] = v_pool[s]
+    return k_out, v_out
+
+
+# ---------------------------------------------------------------------------
 # Decode
 # ---------------------------------------------------------------------------
 

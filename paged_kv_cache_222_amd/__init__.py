@@ -13,6 +13,7 @@ from ._binding import (  # noqa: F401
     PaError,
     load,
     pa_cache_write,
+    pa_copy_blocks,
     pa_decode,
     pa_decode_partitioned,
     pa_reduce,

@@ -54,6 +54,8 @@ def load() -> ctypes.CDLL:
         vp, i32, f32 = ctypes.c_void_p, ctypes.c_int32, ctypes.c_float
         lib.pa_cache_write.argtypes = [vp, vp, vp, vp, vp, i32, i32, i32, i32,
                                        i32, i32, vp]
+        lib.pa_copy_blocks.argtypes = [vp, vp, vp, i32, i32, i32, i32, i32,
+                                       i32, vp]
         lib.pa_decode.argtypes = [vp, vp, vp, vp, vp, i32, vp, i32, i32, i32,
                                   i32, i32, i32, f32, i32, vp]
         lib.pa_decode_partitioned.argtypes = [vp, vp, vp, i32, i32, vp, vp, vp,
@@ -155,6 +157,23 @@ def pa_cache_write(key, value, k_pool, v_pool, slot_mapping, *, stream=None):
         key.data_ptr(), value.data_ptr(), k_pool.data_ptr(), v_pool.data_ptr(),
         slot_mapping.data_ptr(), n, n_kv, d, bs, n_blocks,
         _dtype_code(k_pool), _stream(stream)))
+
+
+def pa_copy_blocks(k_pool, v_pool, block_pairs, *, stream=None):
+    """Copy whole blocks of both pools: block_pairs [n, 2] int32 rows of
+    (source, destination); see include/pa.h."""
+    torch = _torch()
+    lib = load()
+    _dev("k_pool", k_pool, ndim=4)
+    _dev("v_pool", v_pool, ndim=4)
+    n_blocks, n_kv, bs, d = _pool_dims(k_pool, v_pool)
+    _dev("block_pairs", block_pairs, torch.int32, 2)
+    if block_pairs.shape[1] != 2:
+        raise ValueError("block_pairs must be [n, 2] (source, destination)")
+    _check("pa_copy_blocks", lib.pa_copy_blocks(
+        k_pool.data_ptr(), v_pool.data_ptr(), block_pairs.data_ptr(),
+        block_pairs.shape[0], n_kv, d, bs, n_blocks, _dtype_code(k_pool),
+        _stream(stream)))
 
 
 def _attention_common(q, k_pool, v_pool, block_table, context_lens):

@@ -186,6 +186,29 @@ int pa_cache_write(const void* key, const void* value, void* k_pool, void* v_poo
   return launch_status(pa::launch_cache_write(a, (hipStream_t)stream));
 }
 
+int pa_copy_blocks(void* k_pool, void* v_pool, const int32_t* block_pairs, int32_t n_pairs,
+                   int32_t n_kv_heads, int32_t d_head, int32_t block_size, int32_t n_blocks,
+                   int32_t dtype, void* stream) {
+  if (n_pairs < 0) return PA_ERR_SHAPE;
+  if (n_pairs == 0) return PA_OK;
+  if (!k_pool || !v_pool || !block_pairs) return PA_ERR_NULL;
+  if (!dtype_ok(dtype) || !dhead_ok(d_head) || block_shift_of(block_size) < 0)
+    return PA_ERR_UNSUPPORTED;
+  if (n_kv_heads < 1 || n_blocks < 1) return PA_ERR_SHAPE;
+  if (!aligned16(k_pool) || !aligned16(v_pool) || !aligned4(block_pairs)) return PA_ERR_ALIGN;
+  pa::CopyBlocksArgs a{};
+  a.k_pool = k_pool;
+  a.v_pool = v_pool;
+  a.block_pairs = block_pairs;
+  a.n_pairs = n_pairs;
+  a.n_blocks = n_blocks;
+  a.block_bytes = (int64_t)n_kv_heads * block_size * d_head * elem_bytes(dtype);
+  if ((int64_t)n_pairs * 2 * ((a.block_bytes + pa::kCopyChunk - 1) / pa::kCopyChunk) > INT_MAX)
+    return PA_ERR_SHAPE;  // launch grid
+  (void)hipGetLastError();
+  return launch_status(pa::launch_copy_blocks(a, (hipStream_t)stream));
+}
+
 int pa_decode(void* out, const void* q, const void* k_pool, const void* v_pool,
               const int32_t* block_table, int32_t max_blocks, const int32_t* context_lens,
               int32_t batch, int32_t n_kv_heads, int32_t gqa_group, int32_t d_head,

@@ -60,6 +60,19 @@ struct CacheWriteArgs {
   int32_t n_blocks;
 };
 
+constexpr int kCopyThreads = 256;
+constexpr int kCopyUnroll = 4;  // 16-byte loads in flight per thread
+constexpr int64_t kCopyChunk = (int64_t)kCopyThreads * 16 * kCopyUnroll;  // bytes per work group
+
+struct CopyBlocksArgs {
+  void* k_pool;
+  void* v_pool;
+  const int32_t* block_pairs;  // [n_pairs, 2]: source, destination
+  int32_t n_pairs;
+  int32_t n_blocks;
+  int64_t block_bytes;         // n_kv_heads * block_size * d_head * element size
+};
+
 // Each returns a hipError_t from the launch.
 hipError_t launch_attention_f32(const AttnArgs& a, int d_head, int heads_per_chunk,
                                 unsigned grid, hipStream_t s);
@@ -71,6 +84,7 @@ hipError_t launch_attention_mfma_bf16(const AttnArgs& a, int d_head, unsigned gr
 int attention_mfma_occupancy(int dtype, int d_head);
 hipError_t launch_reduce(const ReduceArgs& a, int dtype, int d_head, hipStream_t s);
 hipError_t launch_cache_write(const CacheWriteArgs& a, hipStream_t s);
+hipError_t launch_copy_blocks(const CopyBlocksArgs& a, hipStream_t s);
 
 constexpr int kAttnThreads = 256;  // four waves per work item
 constexpr int kMfmaHeads = 16;     // query heads per work item on the matrix cores

@@ -401,3 +401,24 @@ def make_custom(context_lens, *, n_q_heads: int, n_kv_heads: int, d_head: int,
                  lengths=_fixed(ctx), std=std, pool_blocks=pool_blocks,
                  prefix_len=prefix_len, partition_size=partition_size)
     return make_workload(cfg, seed, poison=poison)
+
+
+def make_copy_pairs(n_blocks: int, n_pairs: int, seed: int = 0, *,
+                    invalid: int = 0) -> np.ndarray:
+    """[n_pairs + invalid, 2] int32 (source, destination) rows for a block
+    copy over a pool of n_blocks: distinct destinations, none of them a
+    source; ``invalid`` extra rows name a block outside the pool."""
+    if 2 * n_pairs > n_blocks:
+        raise ValueError("need 2 * n_pairs <= n_blocks")
+    rng = np.random.default_rng(np.random.SeedSequence(seed).spawn(7)[6])
+    perm = rng.permutation(n_blocks)
+    dst = perm[:n_pairs]
+    src = rng.choice(perm[n_pairs:], size=n_pairs, replace=True)
+    pairs = np.stack([src, dst], axis=1).astype(np.int32)
+    if invalid:
+        bad = np.stack([rng.choice([-1, n_blocks], invalid),
+                        rng.integers(0, n_blocks, invalid)], axis=1)
+        bad[1::2] = bad[1::2, ::-1]          # half with a bad destination
+        pairs = np.concatenate([pairs, bad.astype(np.int32)])
+        pairs = pairs[rng.permutation(len(pairs))]
+    return np.ascontiguousarray(pairs, dtype=np.int32)

@@ -28,8 +28,8 @@ def declared_functions():
 
 def test_header_declares_the_entry_points():
     assert declared_functions() == sorted(
-        ["pa_cache_write", "pa_decode", "pa_decode_partitioned", "pa_reduce",
-         "pa_strerror"])
+        ["pa_cache_write", "pa_copy_blocks", "pa_decode",
+         "pa_decode_partitioned", "pa_reduce", "pa_strerror"])
 
 
 def test_library_exports_every_declared_symbol(lib):
@@ -76,6 +76,30 @@ def test_cache_write_argument_checks(lib):
     assert _cw(lib, nb=0) == PA_ERR_SHAPE
     assert _cw(lib, key=MIS) == PA_ERR_ALIGN
     assert _cw(lib, k_pool=MIS) == PA_ERR_ALIGN
+
+
+def _cb(lib, **kw):
+    a = dict(k_pool=P, v_pool=P, pairs=P, n=4, hkv=2, d=128, bs=16, nb=8,
+             dt=2)
+    a.update(kw)
+    return lib.pa_copy_blocks(a["k_pool"], a["v_pool"], a["pairs"], a["n"],
+                              a["hkv"], a["d"], a["bs"], a["nb"], a["dt"],
+                              None)
+
+
+def test_copy_blocks_argument_checks(lib):
+    assert _cb(lib, n=0) == PA_OK                     # no-op, nothing launched
+    assert _cb(lib, n=-1) == PA_ERR_SHAPE
+    for k in ("k_pool", "v_pool", "pairs"):
+        assert _cb(lib, **{k: None}) == PA_ERR_NULL, k
+    assert _cb(lib, d=48) == PA_ERR_UNSUPPORTED
+    assert _cb(lib, bs=24) == PA_ERR_UNSUPPORTED
+    assert _cb(lib, dt=5) == PA_ERR_UNSUPPORTED
+    assert _cb(lib, hkv=0) == PA_ERR_SHAPE
+    assert _cb(lib, nb=0) == PA_ERR_SHAPE
+    assert _cb(lib, k_pool=MIS) == PA_ERR_ALIGN
+    assert _cb(lib, pairs=P + 2) == PA_ERR_ALIGN
+    assert _cb(lib, n=2**30, hkv=64, bs=64, dt=0) == PA_ERR_SHAPE  # launch grid
 
 
 def _dec(lib, **kw):

@@ -321,6 +321,64 @@ def test_cache_write_matches_flat_slot_view(dtype):
     assert not np.shares_memory(k2, pool_k)
 
 
+def _coded_pools(nb, H, BS, D):
+    """f32 pools whose element (b, h, p, d) stores its own index code
+    ((b*H + h)*BS + p)*D + d in K and -1 - code in V (exact integers)."""
+    code = np.arange(nb * H * BS * D, dtype=np.float64).reshape(nb, H, BS, D)
+    return code.astype(np.float32), (-1.0 - code).astype(np.float32)
+
+
+def test_copy_blocks_moves_whole_blocks():
+    """Pin: decoding the stored codes after the copy, every element of a
+    destination block names the source block at the same (head, position,
+    dimension), in both pools; every other block still names itself; rows
+    with an id outside the pool change nothing."""
+    nb, H, BS, D = 12, 3, 4, 8
+    k0, v0 = _coded_pools(nb, H, BS, D)
+    pairs = np.array([[1, 7], [3, 9], [-1, 2], [4, nb], [11, 0]], np.int32)
+    k2, v2 = oracle.oracle_copy_blocks(k0, v0, pairs)
+    src_of = {7: 1, 9: 3, 0: 11}
+    idx = np.indices((H, BS, D))
+    for b in range(nb):
+        want = src_of.get(b, b)
+        code_k = k2[b].astype(np.int64)
+        code_v = (-1.0 - v2[b].astype(np.float64)).astype(np.int64)
+        for code in (code_k, code_v):
+            dd = code % D
+            pp = (code // D) % BS
+            hh = (code // (D * BS)) % H
+            bb = code // (D * BS * H)
+            assert (bb == want).all(), b
+            assert (hh == idx[0]).all() and (pp == idx[1]).all() and (dd == idx[2]).all()
+    assert not np.shares_memory(k2, k0)
+    assert (k0 == _coded_pools(nb, H, BS, D)[0]).all()     # inputs untouched
+
+
+def test_copy_on_write_keeps_the_attention_output():
+    """Invariant: pointing a sequence's table at copies of its blocks (the
+    copy-on-write step) leaves its attention output bit-identical."""
+    rng = np.random.default_rng(57)
+    ctx = [37, 64, 5]
+    Hq, Hkv, D, BS = 4, 2, 16, 8
+    q, seqs = _draw(rng, ctx, Hq, Hkv, D)
+    k_pool, v_pool, table, ctx_a = _page(rng, seqs, BS, extra_blocks=20)
+    scale = 1.0 / np.sqrt(D)
+    base = oracle.oracle_decode(q, k_pool, v_pool, table, ctx_a, scale,
+                                Hq // Hkv, BS, "f32")
+    used = sorted({int(x) for x in table[table >= 0].ravel()})
+    free = [b for b in range(k_pool.shape[0]) if b not in set(used)]
+    pairs = np.array(list(zip(used, free[:len(used)])), np.int32)
+    k2, v2 = oracle.oracle_copy_blocks(k_pool, v_pool, pairs)
+    remap = dict(zip(used, free[:len(used)]))
+    table2 = np.vectorize(lambda x: remap.get(int(x), x))(table).astype(np.int32)
+    # the originals are overwritten afterwards: only the copies are read
+    k2[used] = np.nan
+    v2[used] = np.nan
+    got = oracle.oracle_decode(q, k2, v2, table2, ctx_a, scale, Hq // Hkv,
+                               BS, "f32")
+    assert np.array_equal(got, base)
+
+
 def test_write_then_single_position_decode_round_trip():
     """Round trip: write a token into an empty pool, decode a 1-position
     sequence over it, get the written value back exactly."""
@@ -470,3 +528,21 @@ def test_planted_cache_write_mistake_is_caught(monkeypatch):
     monkeypatch.setattr(oracle, "oracle_cache_write", bad_write)
     with pytest.raises(AssertionError):
         test_cache_write_matches_flat_slot_view("f32")
+
+
+def test_planted_copy_blocks_mistake_is_caught(monkeypatch):
+    """Copying the destination onto the source, or only the K pool, must
+    fail the code pin."""
+    real = oracle.oracle_copy_blocks
+
+    def reversed_copy(k_pool, v_pool, pairs):
+        return real(k_pool, v_pool, np.asarray(pairs)[:, ::-1].copy())
+
+    def k_only(k_pool, v_pool, pairs):
+        k2, _ = real(k_pool, v_pool, pairs)
+        return k2, v_pool.copy()
+
+    for bad in (reversed_copy, k_only):
+        monkeypatch.setattr(oracle, "oracle_copy_blocks", bad)
+        with pytest.raises(AssertionError):
+            test_copy_blocks_moves_whole_blocks()
