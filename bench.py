@@ -53,9 +53,14 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
                     help="budget of the CPU oracle sample")
-    ap.add_argument("--op", choices=["decode", "copy-blocks"], default="decode",
+    ap.add_argument("--op", choices=["decode", "copy-blocks", "verify"],
+                    default="decode",
                     help="decode: the decode step (default); copy-blocks: "
-                         "the copy-on-write block copy on the LLaMA-3-8B pool")
+                         "the copy-on-write block copy on the LLaMA-3-8B pool; "
+                         "verify: a speculative-decoding verify step, "
+                         "--queries tokens per sequence")
+    ap.add_argument("--queries", type=int, default=4,
+                    help="verify: query tokens per sequence")
     ap.add_argument("--pairs", type=int, default=4096,
                     help="copy-blocks: block pairs per call")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
@@ -210,6 +215,124 @@ def bench_copy_blocks(args, torch, pa, wl):
     print(json.dumps(rec), flush=True)
 
 
+def bench_verify(args, torch, pa, wl):
+    """The verify pass of speculative decoding on the LLaMA-3-8B batch: the
+    cache write of every sequence's last k tokens, then pa_decode_multi
+    (k causal query tokens per sequence) and pa_reduce."""
+    w = wl.make_workload(args.config, seed=args.seed)
+    c = w.cfg
+    k = args.queries
+    P = args.partition_size or c.partition_size
+    pmax = max(1, -(-int(w.context_lens.max()) // P))
+    tdt = {"f16": torch.float16, "bf16": torch.bfloat16}[c.dtype]
+
+    def up(x, dt=None):
+        if dt is not None:
+            return torch.from_numpy(x.view(np.int16)).view(dt).cuda()
+        return torch.from_numpy(np.ascontiguousarray(x)).cuda()
+
+    qm = wl.make_multi_queries(w, k, seed=args.seed)
+    slots = up(wl.multi_token_slots(w, k))
+    rng = np.random.default_rng(args.seed + 7)
+    kv_new = wl.encode(rng.standard_normal(
+        (c.batch * k, c.n_kv_heads, c.d_head), dtype=np.float32), c.dtype)
+    copies = [dict(k=up(w.k_pool, tdt), v=up(w.v_pool, tdt), q=up(qm, tdt),
+                   kn=up(kv_new, tdt), vn=up(kv_new, tdt))
+              for _ in range(args.copies)]
+    tbl, cl = up(w.block_table), up(w.context_lens)
+    B, Hq, D = c.batch, c.n_q_heads, c.d_head
+    ws = pa.partition_workspace(B, k * Hq, D, pmax)
+    out = torch.empty((B, k, Hq, D), dtype=tdt, device="cuda")
+    stream = torch.cuda.current_stream()
+
+    def step(x, ev=None):
+        if ev is not None:
+            ev[0].record(stream)
+        pa.pa_cache_write(x["kn"], x["vn"], x["k"], x["v"], slots)
+        if ev is not None:
+            ev[1].record(stream)
+        pa.pa_decode_multi(*ws, x["q"], x["k"], x["v"], tbl, cl,
+                           partition_size=P, scale=w.scale)
+        if ev is not None:
+            ev[2].record(stream)
+        pa.pa_reduce(out.view(B, k * Hq, D), *ws, cl, partition_size=P)
+        if ev is not None:
+            ev[3].record(stream)
+
+    for i in range(args.warmup):
+        step(copies[i % len(copies)])
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(copies[i % len(copies)])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)]
+           for _ in range(args.steps)]
+    for i in range(args.steps):
+        step(copies[i % len(copies)], evs[i])
+    torch.cuda.synchronize()
+    per = np.array([[e[0].elapsed_time(e[1]), e[1].elapsed_time(e[2]),
+                     e[2].elapsed_time(e[3])] for e in evs]) * 1e3
+    ms = wall / args.steps * 1e3
+    kv = w.kv_bytes_logical()
+    attn_us = float(per[:, 1].mean())
+    nb = 2
+    alg = kv + B * k * Hq * D * nb + 4 * int(
+        (-(-w.context_lens.astype(np.int64) // c.block_size)).sum()) + 4 * B
+    rec = {
+        "metric": "speculative verify step KV-read GB/s (k query tokens per "
+                  "sequence, % of 8 TB/s HBM peak)",
+        "value": round(kv / (ms * 1e-3) / 1e9, 2), "unit": "GB/s",
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": round(ms, 5), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": c.dtype,
+        "data": "synthetic",
+        "config": {"workload": f"{c.name} verify step: cache write of the "
+                               f"last {k} tokens + {k}-token causal attention, "
+                               f"one layer: {c.description}",
+                   "batch": B, "queries": k, "n_q_heads": Hq,
+                   "n_kv_heads": c.n_kv_heads, "d_head": D,
+                   "block_size": c.block_size, "partition_size": P,
+                   "sum_context": int(w.context_lens.sum()), "seed": args.seed},
+        "tokens_per_s": round(B * k / (ms * 1e-3), 1),
+        "kernel_us": {"cache_write": round(float(per[:, 0].mean()), 2),
+                      "attention": round(attn_us, 2),
+                      "reduce": round(float(per[:, 2].mean()), 2)},
+        "roofline": {"kernel": "attention_mfma_kernel (pa_decode_multi)",
+                     "bound": "hbm",
+                     "achieved": round(alg / (attn_us * 1e-6) / 1e9, 1),
+                     "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(alg / (attn_us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
+                     "traffic": None, "algorithmic_bytes_per_launch": alg,
+                     "avg_launch_us": round(attn_us, 3)},
+    }
+    if not args.no_cpu_baseline:
+        import oracle
+        k_ref, v_ref = oracle.oracle_cache_write(w.k_pool, w.v_pool,
+                                                 w.key_new, w.value_new,
+                                                 w.slot_mapping, c.block_size)
+        t0 = time.perf_counter()
+        done, kvb = 0, 0
+        for b in range(B):
+            oracle.oracle_decode_multi(qm, k_ref, v_ref, w.block_table,
+                                       w.context_lens, w.scale, c.gqa_group,
+                                       c.block_size, c.dtype,
+                                       rows=[(b, j, h) for j in range(k)
+                                             for h in range(Hq)])
+            done += 1
+            kvb += int(w.context_lens[b]) * c.n_kv_heads * D * 2 * nb
+            if time.perf_counter() - t0 > args.cpu_seconds:
+                break
+        dt = time.perf_counter() - t0
+        rec["cpu_baseline"] = {
+            "value": round(kvb / dt / 1e9, 4), "unit": "GB/s", "cores": 1,
+            "kind": "oracle",
+            "sample": f"first {done} of {B} sequences, all {k} tokens and "
+                      f"{Hq} heads, fp64 numpy, {dt:.1f} s"}
+    print(json.dumps(rec), flush=True)
+
+
 def cpu_baseline(w, budget_s):
     """The fp64 oracle on the host cores, over the first sequences of the
     batch (all query heads) until the time budget is spent."""
@@ -264,6 +387,9 @@ def main():
     pa.load()
     if args.op == "copy-blocks":
         bench_copy_blocks(args, torch, pa, wl)
+        return
+    if args.op == "verify":
+        bench_verify(args, torch, pa, wl)
         return
     kw = {}
     if args.block_size:

@@ -163,12 +163,43 @@ int pa_decode_partitioned(float* max_logits, float* exp_sums, float* tmp_out,
                           float scale, int32_t dtype, void* stream);
 
 /*
+ * pa_decode_multi -- several query tokens per sequence: the last n_queries
+ * positions of each sequence, causal among themselves, as in the one pass
+ * in which the target model checks all drafted tokens of speculative
+ * decoding ("Serving", section 23.5).  Their keys and values are already in
+ * the cache, and context_lens[b] = n counts them.  Query token j < n_queries
+ * of head h sees the positions t < n - n_queries + j + 1:
+ *   s_t = scale * <q[b, j, h, :], K_t>,  out[b, j, h, :] = sum_t softmax(s)_t V_t
+ * A token that sees no position gives a zero row.  Computed like
+ * pa_decode_partitioned, with n_queries * n_q_heads rows per sequence, row
+ * j * n_q_heads + h; pa_reduce with n_q_heads = n_queries * n_kv_heads *
+ * gqa_group merges them into out viewed as [batch, n_queries * n_q_heads,
+ * d_head].  The KV bytes are read once for all n_queries tokens.
+ *
+ *   q              [batch, n_queries, n_kv_heads * gqa_group, d_head] dtype
+ *   max_logits, exp_sums [batch, n_queries * n_q_heads, max_partitions] f32
+ *   tmp_out   [batch, n_queries * n_q_heads, max_partitions, d_head]    f32
+ *   A (row, partition) that the token's causal limit leaves empty gets
+ *   exp_sums = 0 and tmp_out = 0.  fp16 and bf16 only (PA_ERR_UNSUPPORTED
+ *   for fp32 with n_queries > 1).  Other arguments as in
+ *   pa_decode_partitioned.
+ */
+int pa_decode_multi(float* max_logits, float* exp_sums, float* tmp_out,
+                    int32_t partition_size, int32_t max_partitions,
+                    const void* q, const void* k_pool, const void* v_pool,
+                    const int32_t* block_table, int32_t max_blocks,
+                    const int32_t* context_lens, int32_t batch,
+                    int32_t n_queries, int32_t n_kv_heads, int32_t gqa_group,
+                    int32_t d_head, int32_t block_size, int32_t n_blocks,
+                    float scale, int32_t dtype, void* stream);
+
+/*
  * pa_reduce -- merge per-partition statistics into the attention output.
  * With n_p = ceil(n / partition_size), M = max_{p<n_p} m_p and
  * w_p = l_p * exp(m_p - M):
  *   out[b, h, :] = sum_p w_p tmp_out[b, h, p, :] / sum_p w_p
- * n == 0 gives a zero row.  Arrays as in pa_decode_partitioned; out as in
- * pa_decode.
+ * n == 0 gives a zero row (and so does a row whose partitions all have
+ * exp_sums = 0).  Arrays as in pa_decode_partitioned; out as in pa_decode.
  */
 int pa_reduce(void* out, const float* max_logits, const float* exp_sums,
               const float* tmp_out, const int32_t* context_lens, int32_t batch,

@@ -10,6 +10,7 @@ from .paged_attention import (  # noqa: F401
     oracle_cache_write,
     oracle_copy_blocks,
     oracle_decode,
+    oracle_decode_multi,
     oracle_decode_row,
     oracle_merge,
     oracle_partitions,

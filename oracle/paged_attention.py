@@ -192,6 +192,34 @@ def oracle_decode(q, k_pool, v_pool, block_table, context_lens, scale,
     return out
 
 
+def oracle_decode_multi(q, k_pool, v_pool, block_table, context_lens, scale,
+                        gqa_group, block_size, dtype, rows=None) -> np.ndarray:
+    """Several query tokens per sequence, causal among themselves.
+
+    The target model of speculative decoding checks all drafted tokens in one
+    pass ("Serving", §23.5): ``q`` is ``[B, k, n_q_heads, d_head]``, the query
+    of each sequence's last ``k`` positions, whose keys and values are
+    already cached (``context_lens[b] = n`` counts them).  Token ``j`` sits
+    at position ``n - k + j`` and, as in any causal decoder, attends to the
+    positions up to and including its own: ``t < n - k + j + 1``.  A token
+    that sees no position gives a zero row.  ``rows`` optionally lists
+    ``(b, j, h)`` triples to compute (others are NaN).  Returns fp64
+    ``[B, k, n_q_heads, d_head]``."""
+    B, k, Hq, D = q.shape
+    out = np.full((B, k, Hq, D), np.nan)
+    trip = rows if rows is not None else [(b, j, h) for b in range(B)
+                                          for j in range(k) for h in range(Hq)]
+    for b, j, h in trip:
+        visible = int(context_lens[b]) - k + j + 1
+        if visible <= 0:
+            out[b, j, h] = 0.0
+            continue
+        out[b, j, h], _ = oracle_decode_row(
+            q[:, j], k_pool, v_pool, block_table, context_lens, scale,
+            gqa_group, block_size, dtype, b, h, stop=visible)
+    return out
+
+
 # ---------------------------------------------------------------------------
 # Split context: per-partition statistics and their merge
 # ---------------------------------------------------------------------------

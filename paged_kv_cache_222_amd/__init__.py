@@ -15,6 +15,7 @@ from ._binding import (  # noqa: F401
     pa_cache_write,
     pa_copy_blocks,
     pa_decode,
+    pa_decode_multi,
     pa_decode_partitioned,
     pa_reduce,
     pa_strerror,

@@ -56,6 +56,9 @@ def load() -> ctypes.CDLL:
                                        i32, i32, vp]
         lib.pa_copy_blocks.argtypes = [vp, vp, vp, i32, i32, i32, i32, i32,
                                        i32, vp]
+        lib.pa_decode_multi.argtypes = [vp, vp, vp, i32, i32, vp, vp, vp, vp,
+                                        i32, vp, i32, i32, i32, i32, i32, i32,
+                                        i32, f32, i32, vp]
         lib.pa_decode.argtypes = [vp, vp, vp, vp, vp, i32, vp, i32, i32, i32,
                                   i32, i32, i32, f32, i32, vp]
         lib.pa_decode_partitioned.argtypes = [vp, vp, vp, i32, i32, vp, vp, vp,
@@ -63,8 +66,8 @@ def load() -> ctypes.CDLL:
                                               i32, i32, f32, i32, vp]
         lib.pa_reduce.argtypes = [vp, vp, vp, vp, vp, i32, i32, i32, i32, i32,
                                   i32, vp]
-        for fn in ("pa_cache_write", "pa_decode", "pa_decode_partitioned",
-                   "pa_reduce"):
+        for fn in ("pa_cache_write", "pa_copy_blocks", "pa_decode",
+                   "pa_decode_partitioned", "pa_decode_multi", "pa_reduce"):
             getattr(lib, fn).restype = ctypes.c_int
         lib.pa_strerror.argtypes = [ctypes.c_int]
         lib.pa_strerror.restype = ctypes.c_char_p
@@ -230,6 +233,39 @@ def pa_decode_partitioned(max_logits, exp_sums, tmp_out, q, k_pool, v_pool,
         int(partition_size), pmax, q.data_ptr(), k_pool.data_ptr(),
         v_pool.data_ptr(), block_table.data_ptr(), mb, context_lens.data_ptr(),
         B, n_kv, G, d, bs, n_blocks, float(scale), _dtype_code(q),
+        _stream(stream)))
+
+
+def pa_decode_multi(max_logits, exp_sums, tmp_out, q, k_pool, v_pool,
+                    block_table, context_lens, *, partition_size, scale,
+                    stream=None):
+    """Multi-token queries: q [B, k, Hq, D] holds each sequence's last k
+    positions, causal among them.  Per-partition statistics go to the fp32
+    workspace (max_logits/exp_sums [B, k*Hq, PMAX], tmp_out
+    [B, k*Hq, PMAX, D]); pa_reduce on out viewed as [B, k*Hq, D] finishes."""
+    torch = _torch()
+    lib = load()
+    _dev("q", q, ndim=4)
+    B, k, Hq, d = q.shape
+    B, Hq_, n_kv, G, d, bs, n_blocks, mb = _attention_common(
+        q.view(B, k * Hq, d), k_pool, v_pool, block_table, context_lens)
+    if Hq % n_kv != 0:
+        raise ValueError("q must be [B, k, n_kv_heads * G, d_head]")
+    G = Hq // n_kv
+    _dev("max_logits", max_logits, torch.float32, 3)
+    _dev("exp_sums", exp_sums, torch.float32, 3)
+    _dev("tmp_out", tmp_out, torch.float32, 4)
+    pmax = max_logits.shape[2]
+    if (tuple(max_logits.shape) != (B, k * Hq, pmax)
+            or tuple(exp_sums.shape) != (B, k * Hq, pmax)
+            or tuple(tmp_out.shape) != (B, k * Hq, pmax, d)):
+        raise ValueError("workspace shapes must be [B, k*Hq, PMAX] and "
+                         "[B, k*Hq, PMAX, D]")
+    _check("pa_decode_multi", lib.pa_decode_multi(
+        max_logits.data_ptr(), exp_sums.data_ptr(), tmp_out.data_ptr(),
+        int(partition_size), pmax, q.data_ptr(), k_pool.data_ptr(),
+        v_pool.data_ptr(), block_table.data_ptr(), mb, context_lens.data_ptr(),
+        B, k, n_kv, G, d, bs, n_blocks, float(scale), _dtype_code(q),
         _stream(stream)))
 
 

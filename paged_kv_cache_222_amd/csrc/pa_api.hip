@@ -75,6 +75,7 @@ pa::AttnArgs attention_args(const void* q, const void* k_pool, const void* v_poo
   a.batch = batch;
   a.n_kv_heads = n_kv_heads;
   a.gqa_group = gqa_group;
+  a.n_queries = 1;
   int gc, nhc;
   head_chunks(gqa_group, &gc, &nhc);
   a.n_hchunks = nhc;
@@ -118,7 +119,8 @@ hipError_t dispatch_attention(pa::AttnArgs a, int32_t dtype, int32_t d_head, int
     }
     return pa::launch_attention_f32(a, d_head, a.heads_per_chunk, (unsigned)grid, s);
   }
-  a.n_hchunks = (a.gqa_group + pa::kMfmaHeads - 1) / pa::kMfmaHeads;
+  // columns of a KV head: (query token, head of the group) pairs
+  a.n_hchunks = (a.gqa_group * a.n_queries + pa::kMfmaHeads - 1) / pa::kMfmaHeads;
   a.heads_per_chunk = pa::kMfmaHeads;
   const int64_t cols = (int64_t)a.n_kv_heads * a.n_hchunks;
   int64_t grid = rows * cols;
@@ -135,6 +137,44 @@ hipError_t dispatch_attention(pa::AttnArgs a, int32_t dtype, int32_t d_head, int
   }
   return dtype == PA_F16 ? pa::launch_attention_mfma_f16(a, d_head, (unsigned)grid, s)
                          : pa::launch_attention_mfma_bf16(a, d_head, (unsigned)grid, s);
+}
+
+// Shared by pa_decode_partitioned and pa_decode_multi.
+int decode_partitioned(float* max_logits, float* exp_sums, float* tmp_out,
+                       int32_t partition_size, int32_t max_partitions, const void* q,
+                       const void* k_pool, const void* v_pool, const int32_t* block_table,
+                       int32_t max_blocks, const int32_t* context_lens, int32_t batch,
+                       int32_t n_queries, int32_t n_kv_heads, int32_t gqa_group,
+                       int32_t d_head, int32_t block_size, int32_t n_blocks, float scale,
+                       int32_t dtype, void* stream) {
+  if (batch < 0 || n_queries < 1) return PA_ERR_SHAPE;
+  if (batch == 0) return PA_OK;
+  if (!max_logits || !exp_sums || !tmp_out) return PA_ERR_NULL;
+  int st = check_attention(q, k_pool, v_pool, block_table, max_blocks, context_lens, batch,
+                           n_kv_heads, gqa_group, d_head, block_size, n_blocks, dtype);
+  if (st != PA_OK) return st;
+  if (n_queries > 1 && dtype == PA_F32) return PA_ERR_UNSUPPORTED;
+  if ((int64_t)n_queries * n_kv_heads * gqa_group > INT_MAX / 4 ||
+      (int64_t)batch * n_queries * n_kv_heads * gqa_group > INT_MAX / 2)
+    return PA_ERR_SHAPE;
+  if (partition_size <= 0 || partition_size % block_size != 0) return PA_ERR_PARTITION;
+  if (max_partitions < 1) return PA_ERR_WORKSPACE;
+  if (!aligned4(max_logits) || !aligned4(exp_sums) || !aligned16(tmp_out)) return PA_ERR_ALIGN;
+  pa::AttnArgs a = attention_args(q, k_pool, v_pool, block_table, max_blocks, context_lens,
+                                  batch, n_kv_heads, gqa_group, block_size, n_blocks, scale);
+  a.max_logits = max_logits;
+  a.exp_sums = exp_sums;
+  a.tmp_out = tmp_out;
+  a.partition_size = partition_size;
+  a.max_partitions = max_partitions;
+  a.n_queries = n_queries;
+  const int64_t rows = (int64_t)max_partitions * batch;
+  if (rows * n_kv_heads * (((int64_t)gqa_group * n_queries + 7) / 8) > INT_MAX)
+    return PA_ERR_SHAPE;
+  (void)hipGetLastError();
+  int st2 = PA_OK;
+  const hipError_t e = dispatch_attention(a, dtype, d_head, rows, (hipStream_t)stream, &st2);
+  return st2 != PA_OK ? st2 : launch_status(e);
 }
 
 }  // namespace
@@ -232,6 +272,7 @@ int pa_decode(void* out, const void* q, const void* k_pool, const void* v_pool,
   return st2 != PA_OK ? st2 : launch_status(e);
 }
 
+
 int pa_decode_partitioned(float* max_logits, float* exp_sums, float* tmp_out,
                           int32_t partition_size, int32_t max_partitions, const void* q,
                           const void* k_pool, const void* v_pool,
@@ -239,28 +280,22 @@ int pa_decode_partitioned(float* max_logits, float* exp_sums, float* tmp_out,
                           const int32_t* context_lens, int32_t batch, int32_t n_kv_heads,
                           int32_t gqa_group, int32_t d_head, int32_t block_size,
                           int32_t n_blocks, float scale, int32_t dtype, void* stream) {
-  if (batch < 0) return PA_ERR_SHAPE;
-  if (batch == 0) return PA_OK;
-  if (!max_logits || !exp_sums || !tmp_out) return PA_ERR_NULL;
-  int st = check_attention(q, k_pool, v_pool, block_table, max_blocks, context_lens, batch,
-                           n_kv_heads, gqa_group, d_head, block_size, n_blocks, dtype);
-  if (st != PA_OK) return st;
-  if (partition_size <= 0 || partition_size % block_size != 0) return PA_ERR_PARTITION;
-  if (max_partitions < 1) return PA_ERR_WORKSPACE;
-  if (!aligned4(max_logits) || !aligned4(exp_sums) || !aligned16(tmp_out)) return PA_ERR_ALIGN;
-  pa::AttnArgs a = attention_args(q, k_pool, v_pool, block_table, max_blocks, context_lens,
-                                  batch, n_kv_heads, gqa_group, block_size, n_blocks, scale);
-  a.max_logits = max_logits;
-  a.exp_sums = exp_sums;
-  a.tmp_out = tmp_out;
-  a.partition_size = partition_size;
-  a.max_partitions = max_partitions;
-  const int64_t rows = (int64_t)max_partitions * batch;
-  if (rows * n_kv_heads * ((gqa_group + 7) / 8) > INT_MAX) return PA_ERR_SHAPE;
-  (void)hipGetLastError();
-  int st2 = PA_OK;
-  const hipError_t e = dispatch_attention(a, dtype, d_head, rows, (hipStream_t)stream, &st2);
-  return st2 != PA_OK ? st2 : launch_status(e);
+  return decode_partitioned(max_logits, exp_sums, tmp_out, partition_size, max_partitions, q,
+                            k_pool, v_pool, block_table, max_blocks, context_lens, batch, 1,
+                            n_kv_heads, gqa_group, d_head, block_size, n_blocks, scale, dtype,
+                            stream);
+}
+
+int pa_decode_multi(float* max_logits, float* exp_sums, float* tmp_out, int32_t partition_size,
+                    int32_t max_partitions, const void* q, const void* k_pool,
+                    const void* v_pool, const int32_t* block_table, int32_t max_blocks,
+                    const int32_t* context_lens, int32_t batch, int32_t n_queries,
+                    int32_t n_kv_heads, int32_t gqa_group, int32_t d_head, int32_t block_size,
+                    int32_t n_blocks, float scale, int32_t dtype, void* stream) {
+  return decode_partitioned(max_logits, exp_sums, tmp_out, partition_size, max_partitions, q,
+                            k_pool, v_pool, block_table, max_blocks, context_lens, batch,
+                            n_queries, n_kv_heads, gqa_group, d_head, block_size, n_blocks,
+                            scale, dtype, stream);
 }
 
 int pa_reduce(void* out, const float* max_logits, const float* exp_sums,

@@ -211,6 +211,11 @@ __global__ __launch_bounds__(kAttnThreads, PA_MFMA_MIN_BLOCKS) void attention_mf
   const int bs = 1 << a.block_shift;
   const int G = a.gqa_group;
   const int Hq = a.n_kv_heads * G;
+  const int NQ = a.n_queries;  // query tokens per sequence, the last NQ positions
+  // Columns of a KV head's work: pairs (query token j, head g of the group),
+  // column c = j * G + g, in chunks of 16.  Column c of sequence b reads and
+  // writes row (b * NQ + j) * Hq + kvh * G + g of q / out / the workspace,
+  // and sees positions t < ctx - NQ + j + 1 (causal among the NQ tokens).
   const int K = a.n_kv_heads * a.n_hchunks;
   const bool parts = a.partition_size > 0;
   const bool plan = parts && a.persistent;
@@ -350,8 +355,13 @@ __global__ __launch_bounds__(kAttnThreads, PA_MFMA_MIN_BLOCKS) void attention_mf
     // a scalar read (the table and lengths are not written by this kernel)
     const int ctx = ((const __attribute__((address_space(4))) int32_t*)a.context_lens)[b];
     const bool bad_ctx = ctx < 0 || (int64_t)ctx > max_ctx;
-    const int h0 = kvh * G + hc * 16;
-    const int gv = min(16, G - hc * 16);
+    const int c0 = hc * 16;                // first column of the chunk
+    const int gv = min(16, G * NQ - c0);   // columns in the chunk
+    // row of column c0 + g (see above)
+    auto row_of = [&](int g) -> int64_t {
+      const int c = c0 + g;
+      return (int64_t)(b * NQ + c / G) * Hq + kvh * G + c % G;
+    };
     int t0 = 0, t1 = ctx;
     if (parts) {
       const int64_t np = ctx > 0 ? ((int64_t)ctx + P - 1) / P : 0;
@@ -367,7 +377,7 @@ __global__ __launch_bounds__(kAttnThreads, PA_MFMA_MIN_BLOCKS) void attention_mf
       if (bad_ctx) {
         for (int idx = threadIdx.x; idx < gv * D; idx += kAttnThreads) {
           const int g = idx / D, d = idx - g * D;
-          const int64_t prow = (int64_t)(b * Hq + h0 + g) * a.max_partitions + p;
+          const int64_t prow = row_of(g) * a.max_partitions + p;
           a.tmp_out[prow * D + d] = qnan;
           if (d == 0) {
             a.max_logits[prow] = qnan;
@@ -382,7 +392,7 @@ __global__ __launch_bounds__(kAttnThreads, PA_MFMA_MIN_BLOCKS) void attention_mf
       const float v = bad_ctx ? qnan : 0.0f;
       for (int idx = threadIdx.x; idx < gv * D; idx += kAttnThreads) {
         const int g = idx / D, d = idx - g * D;
-        store_elem<DT>(a.out, (int64_t)(b * Hq + h0 + g) * D + d, v);
+        store_elem<DT>(a.out, row_of(g) * D + d, v);
       }
       continue;
     }
@@ -390,7 +400,7 @@ __global__ __launch_bounds__(kAttnThreads, PA_MFMA_MIN_BLOCKS) void attention_mf
     // ---- queries of the chunk: B operand of S = K Q^T (zero past the group)
     u32x4 qop[KQ];
     {
-      const char* qrow = (const char*)a.q + (int64_t)(b * Hq + h0 + l16) * RB + lg * 16;
+      const char* qrow = (const char*)a.q + row_of(min(l16, gv - 1)) * RB + lg * 16;
 #pragma unroll
       for (int kk = 0; kk < KQ; ++kk)
         qop[kk] = l16 < gv ? *(const u32x4*)(qrow + kk * 64) : u32x4{0u, 0u, 0u, 0u};
@@ -399,6 +409,8 @@ __global__ __launch_bounds__(kAttnThreads, PA_MFMA_MIN_BLOCKS) void attention_mf
     t0 = __builtin_amdgcn_readfirstlane(t0);
     t1 = __builtin_amdgcn_readfirstlane(t1);
     const int ntile = (t1 - t0 + 15) >> 4;
+    const int lim_min = ctx - NQ + 1;                      // of the first query token
+    const int lim_lane = lim_min + (c0 + l16) / G;         // of this lane's column
     const int my_n = __builtin_amdgcn_readfirstlane(ntile > wave ? (ntile - 1 - wave) / NW + 1 : 0);
     const int64_t head_bytes = (int64_t)bs * RB;        // one (block, KV head) tile
     const int64_t blk_bytes = head_bytes * a.n_kv_heads;
@@ -460,7 +472,9 @@ __global__ __launch_bounds__(kAttnThreads, PA_MFMA_MIN_BLOCKS) void attention_mf
     f32x4_t O[ND];
 #pragma unroll
     for (int n = 0; n < ND; ++n) O[n] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-    float m = -__builtin_huge_valf();  // running max (log2 units) of head l16
+    // running max (log2 units) of column l16; a finite floor, so a column
+    // with no visible position yet gives exp2(-inf - m) = 0, not NaN
+    float m = -1e30f;
     float lsum = 0.0f;                 // this lane's share of the normaliser
     // LDS byte addresses of this lane's reads in slot 0 (slot 1 adds an
     // immediate offset): K as the A operand (row l16, chunk 4kk + lg of the
@@ -486,9 +500,11 @@ __global__ __launch_bounds__(kAttnThreads, PA_MFMA_MIN_BLOCKS) void attention_mf
       float x[4];
 #pragma unroll
       for (int j = 0; j < 4; ++j) x[j] = s[j] * sl2;
-      if (nvalid < 16) {
+      if (nvalid < 16 || tok + 16 > lim_min) {
+        // past the item's end, or past this column's causal limit
+        const int nv = min(nvalid, lim_lane - tok);
 #pragma unroll
-        for (int j = 0; j < 4; ++j) x[j] = (lg * 4 + j < nvalid) ? x[j] : -__builtin_huge_valf();
+        for (int j = 0; j < 4; ++j) x[j] = (lg * 4 + j < nv) ? x[j] : -__builtin_huge_valf();
       }
       float bm = fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3]));
       bm = fmaxf(bm, shfl_xor_f(bm, 16));
@@ -590,20 +606,20 @@ __global__ __launch_bounds__(kAttnThreads, PA_MFMA_MIN_BLOCKS) void attention_mf
 #pragma unroll
       for (int w = 0; w < NW; ++w) {
         const float mw = s_m[w][g];
-        const float aw = (mw == -__builtin_huge_valf()) ? 0.0f : exp2_fast(mw - M);
+        const float aw = exp2_fast(mw - M);  // waves without positions have l = 0
         L += aw * s_l[w][g];
         Ov += aw * s_o[(w * 16 + g) * D + d];
       }
-      const int h = h0 + g;
       if (parts) {
-        const int64_t prow = (int64_t)(b * Hq + h) * a.max_partitions + p;
-        a.tmp_out[prow * D + d] = anybad ? qnan : Ov / L;
+        // a column with no visible position in the partition: l = 0, o = 0
+        const int64_t prow = row_of(g) * a.max_partitions + p;
+        a.tmp_out[prow * D + d] = anybad ? qnan : (L > 0.0f ? Ov / L : 0.0f);
         if (d == 0) {
           a.max_logits[prow] = anybad ? qnan : M * kLn2;
           a.exp_sums[prow] = anybad ? qnan : L;
         }
       } else {
-        store_elem<DT>(a.out, (int64_t)(b * Hq + h) * D + d,
+        store_elem<DT>(a.out, row_of(g) * D + d,
                        anybad ? qnan : (L > 0.0f ? Ov / L : 0.0f));
       }
     }

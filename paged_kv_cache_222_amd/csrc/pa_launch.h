@@ -32,6 +32,7 @@ struct AttnArgs {
   int32_t partition_size;
   int32_t max_partitions;
   int32_t persistent;  // partitioned launch sized to the GPU, items planned in-kernel
+  int32_t n_queries;   // query tokens per sequence (the last n_queries positions)
   float scale_log2;    // scale * log2(e)
 };
 

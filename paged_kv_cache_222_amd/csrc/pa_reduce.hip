@@ -72,7 +72,10 @@ __global__ __launch_bounds__(kWave) void reduce_kernel(ReduceArgs a) {
     }
   }
 #pragma unroll
-  for (int k = 0; k < DPL; ++k) store_elem<DT>(a.out, orow + lane * DPL + k, acc[k] / W);
+  // W = 0: a query token that sees no position (multi-token queries only);
+  // a NaN W (a partition flagged bad) stays NaN
+  for (int k = 0; k < DPL; ++k)
+    store_elem<DT>(a.out, orow + lane * DPL + k, W == 0.0f ? 0.0f : acc[k] / W);
 }
 
 template <Dt DT>

@@ -422,3 +422,32 @@ def make_copy_pairs(n_blocks: int, n_pairs: int, seed: int = 0, *,
         pairs = np.concatenate([pairs, bad.astype(np.int32)])
         pairs = pairs[rng.permutation(len(pairs))]
     return np.ascontiguousarray(pairs, dtype=np.int32)
+
+
+def make_multi_queries(w: Workload, n_queries: int, seed: int = 0) -> np.ndarray:
+    """[B, n_queries, n_q_heads, d_head] queries for the last n_queries
+    positions of each sequence (float32 normals times the batch's std,
+    rounded to its dtype), from a stream of their own."""
+    c = w.cfg
+    rng = np.random.Generator(np.random.PCG64DXSM(
+        np.random.SeedSequence(seed).spawn(8)[7]))
+    x = rng.standard_normal((c.batch, n_queries, c.n_q_heads, c.d_head),
+                            dtype=np.float32)
+    if c.std != 1.0:
+        x *= np.float32(c.std)
+    return encode(x, c.dtype)
+
+
+def multi_token_slots(w: Workload, n_queries: int) -> np.ndarray:
+    """[B * n_queries] int32 flat slots of each sequence's last n_queries
+    positions (the tokens a verify pass writes; -1 below position 0)."""
+    c = w.cfg
+    out = np.full((c.batch, n_queries), -1, dtype=np.int64)
+    for b in range(c.batch):
+        n = int(w.context_lens[b])
+        for j in range(n_queries):
+            pos = n - n_queries + j
+            if pos >= 0:
+                out[b, j] = int(w.block_table[b, pos // c.block_size]) * \
+                    c.block_size + pos % c.block_size
+    return out.reshape(-1).astype(np.int32)

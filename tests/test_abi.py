@@ -28,7 +28,7 @@ def declared_functions():
 
 def test_header_declares_the_entry_points():
     assert declared_functions() == sorted(
-        ["pa_cache_write", "pa_copy_blocks", "pa_decode",
+        ["pa_cache_write", "pa_copy_blocks", "pa_decode", "pa_decode_multi",
          "pa_decode_partitioned", "pa_reduce", "pa_strerror"])
 
 
@@ -150,6 +150,30 @@ def test_partitioned_argument_checks(lib):
     assert _part(lib, d=256) == PA_ERR_UNSUPPORTED
     assert _part(lib, to=MIS) == PA_ERR_ALIGN
     assert _part(lib, pmax=2**20, B=2**12) == PA_ERR_SHAPE   # grid too large
+
+
+def _multi(lib, **kw):
+    a = dict(ml=P, es=P, to=P, psz=512, pmax=4, q=P, k=P, v=P, tbl=P, mb=64,
+             ctx=P, B=4, nq=4, hkv=2, G=4, d=128, bs=16, nb=32, scale=0.1,
+             dt=2)
+    a.update(kw)
+    return lib.pa_decode_multi(
+        a["ml"], a["es"], a["to"], a["psz"], a["pmax"], a["q"], a["k"],
+        a["v"], a["tbl"], a["mb"], a["ctx"], a["B"], a["nq"], a["hkv"],
+        a["G"], a["d"], a["bs"], a["nb"], a["scale"], a["dt"], None)
+
+
+def test_multi_argument_checks(lib):
+    assert _multi(lib, B=0) == PA_OK
+    assert _multi(lib, nq=0) == PA_ERR_SHAPE
+    for k in ("ml", "es", "to", "q", "k", "v", "tbl", "ctx"):
+        assert _multi(lib, **{k: None}) == PA_ERR_NULL, k
+    assert _multi(lib, dt=0) == PA_ERR_UNSUPPORTED        # fp32, k > 1
+    assert _multi(lib, d=96) == PA_ERR_UNSUPPORTED
+    assert _multi(lib, psz=24) == PA_ERR_PARTITION
+    assert _multi(lib, pmax=0) == PA_ERR_WORKSPACE
+    assert _multi(lib, to=MIS) == PA_ERR_ALIGN
+    assert _multi(lib, nq=2**20, B=2**12) == PA_ERR_SHAPE  # rows overflow
 
 
 def _red(lib, **kw):

@@ -1,0 +1,138 @@
+"""pa_decode_multi (several causal query tokens per sequence, the verify pass
+of speculative decoding) + pa_reduce vs the fp64 oracle, through the C ABI
+(needs an MI355X).  Every output element within the stated max-abs-error on
+small ragged batches (sequences shorter than the token count included), on
+sampled rows of the LLaMA-3-8B batch with 4 tokens, and the edge cases:
+one token equals pa_decode_partitioned bit for bit, and a partition beyond a
+token's causal limit is written as empty."""
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from helpers import (TOL, TORCH_DT, as_f64, from_dev, note,
+                     oracle_pools_after_write, rounding_bound, to_dev)
+from paged_kv_cache_222_amd import workloads as wl
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def pa():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import paged_kv_cache_222_amd as pa
+    pa.load()
+    return pa
+
+
+def run_multi(pa, w, qm, k_ref, v_ref, P, name):
+    c = w.cfg
+    B, k, Hq, D = qm.shape
+    pm = max(1, -(-int(w.context_lens.max()) // P))
+    kd, vd = to_dev(k_ref, c.dtype), to_dev(v_ref, c.dtype)
+    qd = to_dev(qm, c.dtype)
+    tbl, cl = to_dev(w.block_table), to_dev(w.context_lens)
+    ws = pa.partition_workspace(B, k * Hq, D, pm)
+    for t in ws:
+        t.fill_(float("nan"))
+    note(f"pa_decode_multi+pa_reduce {name} k={k} P={P} PMAX={pm}")
+    pa.pa_decode_multi(*ws, qd, kd, vd, tbl, cl, partition_size=P,
+                       scale=w.scale)
+    out = torch.full((B, k, Hq, D), float("nan"), dtype=TORCH_DT[c.dtype],
+                     device="cuda")
+    pa.pa_reduce(out.view(B, k * Hq, D), *ws, cl, partition_size=P)
+    torch.cuda.synchronize()
+    return out, ws
+
+
+SMALL = [  # dtype, D, BS, Hkv, G, k, P
+    ("bf16", 128, 16, 2, 4, 4, 64), ("bf16", 128, 16, 1, 4, 4, 512),
+    ("f16", 64, 8, 2, 1, 4, 64), ("bf16", 128, 32, 1, 8, 4, 128),
+    ("f16", 128, 16, 2, 6, 3, 64), ("bf16", 64, 16, 3, 2, 5, 16),
+    ("bf16", 128, 16, 1, 16, 2, 512), ("f16", 128, 64, 2, 3, 1, 128)]
+CTX = [1, 2, 3, 4, 5, 15, 16, 17, 33, 64, 65, 100, 129, 513, 1000]
+
+
+@pytest.mark.parametrize("dtype,D,BS,Hkv,G,k,P", SMALL)
+def test_multi_query_small(pa, dtype, D, BS, Hkv, G, k, P):
+    w = wl.make_custom(CTX, n_q_heads=Hkv * G, n_kv_heads=Hkv, d_head=D,
+                       block_size=BS, dtype=dtype, seed=D + G + k)
+    k_ref, v_ref = oracle_pools_after_write(w)
+    qm = wl.make_multi_queries(w, k, seed=k)
+    out, _ = run_multi(pa, w, qm, k_ref, v_ref, P, f"{dtype} D{D} G{G}")
+    c = w.cfg
+    ref = oracle.oracle_decode_multi(qm, k_ref, v_ref, w.block_table,
+                                     w.context_lens, w.scale, c.gqa_group,
+                                     c.block_size, c.dtype)
+    got = as_f64(out)
+    bound = TOL[dtype] + rounding_bound(ref, dtype)
+    err = np.abs(got - ref)
+    print(f"{dtype} D{D} BS{BS} G{G} k{k} P{P}: max err {err.max():.3g}")
+    assert (err <= bound).all()
+
+
+def test_multi_query_llama3_sampled_rows(pa):
+    """The LLaMA-3-8B batch (B=128, 32/8 heads, d128, bf16, log-normal
+    lengths) with 4 query tokens at partition 2048: every token and head of
+    8 sequences, the longest and the shortest among them."""
+    w = wl.make_workload("llama3-8b", seed=0)
+    c = w.cfg
+    k_ref, v_ref = oracle_pools_after_write(w)
+    qm = wl.make_multi_queries(w, 4, seed=0)
+    out, _ = run_multi(pa, w, qm, k_ref, v_ref, c.partition_size, "llama3-8b")
+    ctx = w.context_lens
+    rng = np.random.default_rng(5)
+    seqs = {int(np.argmax(ctx)), int(np.argmin(ctx))}
+    seqs |= {int(b) for b in rng.choice(c.batch, 6, replace=False)}
+    rows = [(b, j, h) for b in sorted(seqs) for j in range(4)
+            for h in range(c.n_q_heads)]
+    ref = oracle.oracle_decode_multi(qm, k_ref, v_ref, w.block_table, ctx,
+                                     w.scale, c.gqa_group, c.block_size,
+                                     c.dtype, rows=rows)
+    got = as_f64(out)
+    idx = tuple(np.array(rows).T)
+    err = float(np.max(np.abs(got[idx] - ref[idx])))
+    print(f"llama3-8b k=4: max err {err:.3g} over {len(rows)} rows")
+    assert err <= TOL[c.dtype]
+
+
+def test_one_token_equals_partitioned_decode(pa):
+    w = wl.make_custom([5, 40, 300, 777], n_q_heads=8, n_kv_heads=2,
+                       d_head=128, block_size=16, dtype="bf16", seed=3)
+    k_ref, v_ref = oracle_pools_after_write(w)
+    qm = w.q[:, None]
+    out, ws = run_multi(pa, w, qm, k_ref, v_ref, 64, "k=1")
+    B, Hq, D = w.q.shape
+    ws2 = pa.partition_workspace(B, Hq, D, ws[0].shape[2])
+    qd, kd, vd = (to_dev(x, "bf16") for x in (w.q, k_ref, v_ref))
+    tbl, cl = to_dev(w.block_table), to_dev(w.context_lens)
+    note("pa_decode_partitioned+pa_reduce k=1 reference")
+    pa.pa_decode_partitioned(*ws2, qd, kd, vd, tbl, cl, partition_size=64,
+                             scale=w.scale)
+    out2 = torch.empty_like(qd)
+    pa.pa_reduce(out2, *ws2, cl, partition_size=64)
+    torch.cuda.synchronize()
+    assert torch.equal(out[:, 0].view(torch.int16), out2.view(torch.int16))
+
+
+def test_partition_beyond_causal_limit_is_empty(pa):
+    """ctx = 65 at partition 64 with 4 tokens: position 64 is the last
+    token's own; tokens 0-2 see none of partition 1, which must read as
+    empty (exp_sums 0, tmp_out 0)."""
+    w = wl.make_custom([65], n_q_heads=4, n_kv_heads=1, d_head=64,
+                       block_size=16, dtype="f16", seed=9)
+    k_ref, v_ref = oracle_pools_after_write(w)
+    qm = wl.make_multi_queries(w, 4, seed=1)
+    out, ws = run_multi(pa, w, qm, k_ref, v_ref, 64, "causal edge")
+    es = from_dev(ws[1])[0]       # [4 * Hq, PMAX]
+    to = from_dev(ws[2])[0]
+    Hq = 4
+    for j in range(4):
+        rows = slice(j * Hq, (j + 1) * Hq)
+        if j < 3:
+            assert (es[rows, 1] == 0).all() and (to[rows, 1] == 0).all()
+        else:
+            assert (es[rows, 1] > 0).all()
+        assert (es[rows, 0] > 0).all()

@@ -101,6 +101,63 @@ def test_paged_equals_contiguous_sdpa(ctx, Hq, Hkv, D, BS):
     np.testing.assert_allclose(got, ref, rtol=0, atol=1e-12)
 
 
+def _sdpa_multi_reference(q, seqs, scale, G):
+    """torch CPU fp64 SDPA for k query tokens per sequence with an explicit
+    mask: token j (position n - k + j) may attend to keys t <= n - k + j."""
+    B, k, Hq, D = q.shape
+    out = np.zeros((B, k, Hq, D))
+    for b, (K, V) in enumerate(seqs):
+        n = K.shape[1]
+        qt = torch.from_numpy(np.ascontiguousarray(q[b].transpose(1, 0, 2))[None])
+        Kt = torch.from_numpy(np.repeat(K, G, axis=0)[None])     # [1,Hq,n,D]
+        Vt = torch.from_numpy(np.repeat(V, G, axis=0)[None])
+        j = torch.arange(k)[:, None]
+        t = torch.arange(n)[None, :]
+        mask = t <= (n - k + j)                                   # [k, n]
+        o = F.scaled_dot_product_attention(qt, Kt, Vt, attn_mask=mask,
+                                           scale=scale)
+        out[b] = o[0].numpy().transpose(1, 0, 2)
+    return out
+
+
+@pytest.mark.parametrize("ctx,Hq,Hkv,D,BS,k", [
+    ([5, 17, 40], 4, 2, 8, 4, 4), ([33, 64, 4], 8, 2, 16, 16, 4),
+    ([100, 7], 4, 4, 8, 8, 3), ([31, 2], 6, 2, 8, 32, 2)])
+def test_multi_query_equals_masked_sdpa(ctx, Hq, Hkv, D, BS, k):
+    """Pin (library routine): k causal query tokens per sequence equal
+    torch's fp64 SDPA with the bottom-right causal mask."""
+    rng = np.random.default_rng(sum(ctx) + k)
+    q, pk, pv, table, cl, seqs = _contiguous_case(rng, ctx, Hq, Hkv, D, BS)
+    qm = rng.standard_normal((len(ctx), k, Hq, D))
+    scale = 1.0 / math.sqrt(D)
+    got = oracle.oracle_decode_multi(qm, pk, pv, table, cl, scale, Hq // Hkv,
+                                     BS, "f32")
+    ref = _sdpa_multi_reference(qm, seqs, float(np.float32(scale)), Hq // Hkv)
+    np.testing.assert_allclose(got, ref, rtol=0, atol=1e-12)
+
+
+def test_multi_query_single_token_is_decode():
+    """Special case: one query token is single-token decode."""
+    rng = np.random.default_rng(61)
+    q, pk, pv, table, cl, _ = _contiguous_case(rng, [9, 30], 4, 2, 8, 8)
+    got = oracle.oracle_decode_multi(q[:, None], pk, pv, table, cl, 0.3, 2, 8,
+                                     "f32")
+    want = oracle.oracle_decode(q, pk, pv, table, cl, 0.3, 2, 8, "f32")
+    assert np.array_equal(got[:, 0], want)
+
+
+def test_multi_query_token_without_positions_is_zero():
+    """A sequence shorter than k: its first tokens see nothing (zero rows),
+    the rest see a causal prefix."""
+    rng = np.random.default_rng(67)
+    q, pk, pv, table, cl, seqs = _contiguous_case(rng, [2], 2, 1, 4, 4)
+    qm = rng.standard_normal((1, 4, 2, 4))
+    got = oracle.oracle_decode_multi(qm, pk, pv, table, cl, 0.5, 2, 4, "f32")
+    assert (got[0, :2] == 0).all()
+    V = seqs[0][1][0]
+    np.testing.assert_allclose(got[0, 2, 0], V[0], rtol=0, atol=1e-15)
+
+
 def test_stress_large_logits_equal_sdpa():
     """Pin: logits of magnitude ~100s (q scaled up) still match SDPA, which
     needs the max subtraction in the softmax."""
@@ -546,3 +603,35 @@ def test_planted_copy_blocks_mistake_is_caught(monkeypatch):
         monkeypatch.setattr(oracle, "oracle_copy_blocks", bad)
         with pytest.raises(AssertionError):
             test_copy_blocks_moves_whole_blocks()
+
+
+def test_planted_multi_query_mistake_is_caught(monkeypatch):
+    """A mask that lets every token see all positions, one that hides the
+    token's own position, or the tokens taken in reverse order must fail the
+    SDPA pin."""
+    real_row = pa_oracle.oracle_decode_row
+
+    def make(shift):
+        def bad(q, k_pool, v_pool, block_table, context_lens, scale, G, BS,
+                dtype, rows=None):
+            B, k, Hq, D = q.shape
+            out = np.zeros((B, k, Hq, D))
+            for b in range(B):
+                for j in range(k):
+                    for h in range(Hq):
+                        n = int(context_lens[b])
+                        stop = {"all": n, "own": n - k + j,
+                                "rev": n - j}[shift]
+                        if stop <= 0:
+                            continue
+                        out[b, j, h], _ = real_row(
+                            q[:, j], k_pool, v_pool, block_table,
+                            context_lens, scale, G, BS, dtype, b, h,
+                            stop=stop)
+            return out
+        return bad
+
+    for shift in ("all", "own", "rev"):
+        monkeypatch.setattr(oracle, "oracle_decode_multi", make(shift))
+        with pytest.raises(AssertionError):
+            test_multi_query_equals_masked_sdpa([33, 64, 4], 8, 2, 16, 16, 4)
