@@ -53,12 +53,15 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
                     help="budget of the CPU oracle sample")
-    ap.add_argument("--op", choices=["decode", "copy-blocks", "verify"],
+    ap.add_argument("--op", choices=["decode", "copy-blocks", "verify",
+                                     "prefix-cache"],
                     default="decode",
                     help="decode: the decode step (default); copy-blocks: "
                          "the copy-on-write block copy on the LLaMA-3-8B pool; "
                          "verify: a speculative-decoding verify step, "
-                         "--queries tokens per sequence")
+                         "--queries tokens per sequence; prefix-cache: the "
+                         "host-side block hashes and prefix mapping of the "
+                         "shared-prefix batch (no GPU)")
     ap.add_argument("--queries", type=int, default=4,
                     help="verify: query tokens per sequence")
     ap.add_argument("--pairs", type=int, default=4096,
@@ -333,6 +336,88 @@ def bench_verify(args, torch, pa, wl):
     print(json.dumps(rec), flush=True)
 
 
+def bench_prefix_cache(args):
+    """Host-side prefix caching on the shared-prefix batch: each of the 256
+    requests (a 2048-token shared prompt + a private suffix U[1, 6144], token
+    ids synthetic) is hashed block by block and mapped onto the pool; the
+    first request creates the shared blocks, the rest hit them.  Also the
+    Serving 23.4 widget under both policies."""
+    import paged_kv_cache_222_amd as pa
+    from paged_kv_cache_222_amd import pool_sim
+    from paged_kv_cache_222_amd import workloads as wl
+    c = wl.CONFIGS["shared-prefix"]
+    bs = c.block_size
+    ctx = wl.draw_lengths(c, args.seed)
+    rng = np.random.default_rng(args.seed + 11)
+    prompt = rng.integers(0, 128000, c.prefix_len).astype(np.int32)
+    reqs = [np.concatenate([prompt, rng.integers(0, 128000, int(n) - c.prefix_len)
+                            .astype(np.int32)]) for n in ctx]
+    n_tok = int(sum(len(r) for r in reqs))
+    blocks_needed = sum(-(-len(r) // bs) for r in reqs)
+
+    def one_pass():
+        pool = pa.pa_pool_create(blocks_needed)
+        hits = 0
+        tables = []
+        for r in reqs:
+            h = pa.pa_block_hashes(r, bs)
+            ids, hit = pa.pa_pool_map_prefix(pool, h)
+            tail = pa.pa_pool_alloc(pool, 1) if len(r) % bs else ids[:0]
+            tables.append(np.concatenate([ids, tail]))
+            hits += hit
+        return hits, tables
+
+    for _ in range(max(1, args.warmup // 5)):
+        one_pass()
+    reps = max(1, args.steps // 20)
+    t0 = time.perf_counter()
+    for _ in range(reps):
+        hits, tables = one_pass()
+    dt = (time.perf_counter() - t0) / reps
+    shared = c.prefix_len // bs
+    assert all((t[:shared] == tables[0][:shared]).all() for t in tables)
+    W = wl.WIDGET
+    a, pr, fi = wl.widget_requests(args.seed)
+    sims = {pol: pool_sim.simulate(a, pr, fi, W["n_blocks"], W["block_size"],
+                                   pol, W["max_len"])
+            for pol in ("reserve", "paged")}
+    rec = {
+        "metric": "prefix-cache mapping requests/s (host, native: block "
+                  "hashes + pool mapping)",
+        "value": round(len(reqs) / dt, 1), "unit": "requests/s",
+        "n_gpus": 0, "steps": reps, "warmup": max(1, args.warmup // 5),
+        "ms_per_step": round(dt * 1e3, 4), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "int32/uint64",
+        "data": "synthetic",
+        "config": {"workload": "shared-prefix batch: 256 requests, 2048-token "
+                               "shared prompt + suffix U[1,6144], 16-token "
+                               "blocks, one pass = hash + map every request",
+                   "requests": len(reqs), "tokens": n_tok, "seed": args.seed},
+        "tokens_hashed_per_s": round(n_tok / dt, 1),
+        "prefix_hits": hits, "blocks_mapped": int(sum(len(t) for t in tables)),
+        "widget": {pol: {"max_running": max(r["running"]),
+                         "starts": r["start"],
+                         "utilisation": round(r["utilisation"], 4)}
+                   for pol, r in sims.items()},
+        "roofline": None,
+    }
+    if not args.no_cpu_baseline:
+        import oracle.block_pool as ob
+        t0 = time.perf_counter()
+        done = 0
+        pool = ob.OraclePool(blocks_needed)
+        while done < len(reqs) and time.perf_counter() - t0 < min(args.cpu_seconds, 10.0):
+            pool.map_prefix(ob.block_hashes(reqs[done].tolist(), bs))
+            done += 1
+        dt2 = time.perf_counter() - t0
+        rec["cpu_baseline"] = {
+            "value": round(done / dt2, 3), "unit": "requests/s", "cores": 1,
+            "kind": "oracle",
+            "sample": f"first {done} of {len(reqs)} requests through the "
+                      f"pure-Python oracle, {dt2:.1f} s"}
+    print(json.dumps(rec), flush=True)
+
+
 def cpu_baseline(w, budget_s):
     """The fp64 oracle on the host cores, over the first sequences of the
     batch (all query heads) until the time budget is spent."""
@@ -374,6 +459,9 @@ def main():
               "no exchange, so N GPUs would run N independent copies)",
               file=sys.stderr)
         sys.exit(2)
+    if args.op == "prefix-cache":
+        bench_prefix_cache(args)
+        return
     import torch
 
     import paged_kv_cache_222_amd as pa

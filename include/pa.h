@@ -16,8 +16,10 @@
  * Conventions for every entry point
  * ---------------------------------
  * - Pointers are DEVICE pointers owned by the caller unless stated otherwise.
- *   The library never allocates, frees or retains memory and keeps no state
- *   between calls, so calls on different streams are independent.
+ *   The GPU entry points never allocate, free or retain memory and keep no
+ *   state between calls, so calls on different streams are independent.
+ *   The host-side block pool (pa_pool_*, pa_block_hashes, at the end) works
+ *   on HOST memory: a pool is an object the caller creates and destroys.
  * - All arrays are dense and row-major, with the shapes given below, and
  *   every array pointer is 16-byte aligned.
  * - q, pools and out share one element type (dtype); partition workspace is
@@ -67,7 +69,8 @@ enum {
   PA_ERR_WORKSPACE = -4,   /* max_partitions < 1 */
   PA_ERR_PARTITION = -5,   /* partition_size not a positive multiple of block_size */
   PA_ERR_HIP = -6,         /* the HIP runtime reported an error at launch */
-  PA_ERR_ALIGN = -7        /* an array pointer is not 16-byte aligned */
+  PA_ERR_ALIGN = -7,       /* an array pointer is not 16-byte aligned */
+  PA_ERR_NOSPACE = -8      /* the block pool has too few free blocks */
 };
 
 /*
@@ -205,6 +208,75 @@ int pa_reduce(void* out, const float* max_logits, const float* exp_sums,
               const float* tmp_out, const int32_t* context_lens, int32_t batch,
               int32_t n_q_heads, int32_t d_head, int32_t partition_size,
               int32_t max_partitions, int32_t dtype, void* stream);
+
+/*
+ * Host-side block pool and prefix cache (HOST pointers; no GPU work).
+ *
+ * The allocator behind the paged cache: blocks are handed out as sequences
+ * grow and shared by sequences with a common prefix ("Serving", section
+ * 23.4), with reference counts so a shared block is released only by its
+ * last user (copy it with pa_copy_blocks before writing into it).  Prefix
+ * caching names each full block by a hash of its tokens chained with the
+ * hash of the block before it (the block-and-hash-chain scheme of the
+ * prompt-caching articles on the pagedattention tag page), so a request
+ * whose leading blocks hash alike reuses their physical blocks, and one
+ * changed token renames every later block.
+ *
+ * Policy (fixed, so results are reproducible): a fresh block is the
+ * lowest-numbered free block holding no cached prefix, else the cached free
+ * block released longest ago (its hash is then forgotten).  A block whose
+ * reference count drops to zero is free; if it carries a hash it stays
+ * findable until it is reused.  A pool is not thread-safe.
+ */
+typedef struct pa_block_pool pa_block_pool;
+
+/*
+ * pa_block_hashes -- chained hashes of the full blocks of a token sequence.
+ * With h_{-1} = parent (0 at the start of a sequence), block i (tokens
+ * [i * block_size, (i + 1) * block_size)) gets
+ *   h_i = FNV-1a-64(8 bytes of h_{i-1}, little endian, then the block's
+ *                   token ids as 4-byte little-endian integers)
+ * (FNV-1a: offset basis 14695981039346656037, prime 1099511628211).
+ * Writes n_full = n_tokens / block_size hashes.
+ *   tokens [n_tokens] int32, hashes [n_tokens / block_size] uint64 (host)
+ */
+int pa_block_hashes(const int32_t* tokens, int32_t n_tokens,
+                    int32_t block_size, uint64_t parent, uint64_t* hashes,
+                    int32_t* n_full);
+
+/* A pool of n_blocks physical block ids, all free; NULL if n_blocks < 1 or
+ * out of memory.  pa_pool_destroy(NULL) is allowed. */
+pa_block_pool* pa_pool_create(int32_t n_blocks);
+void pa_pool_destroy(pa_block_pool* pool);
+
+/* Blocks that can be handed out now (free, cached or not). */
+int32_t pa_pool_available(const pa_block_pool* pool);
+
+/* Reference count of one block (0 = free). */
+int32_t pa_pool_refcount(const pa_block_pool* pool, int32_t block);
+
+/* n fresh blocks with reference count 1 into ids[n]; PA_ERR_NOSPACE (and no
+ * change) if fewer than n are available. */
+int pa_pool_alloc(pa_block_pool* pool, int32_t n, int32_t* ids);
+
+/* One more reference to each listed block (a sequence starts sharing it);
+ * PA_ERR_SHAPE (and no change) if any is out of range or free. */
+int pa_pool_fork(pa_block_pool* pool, const int32_t* ids, int32_t n);
+
+/* One reference fewer for each listed block (a block may be listed as many
+ * times as it has references); PA_ERR_SHAPE (and no change) otherwise. */
+int pa_pool_release(pa_block_pool* pool, const int32_t* ids, int32_t n);
+
+/*
+ * pa_pool_map_prefix -- physical blocks for a request's full blocks, given
+ * their chained hashes.  The longest leading run of hashes found in the
+ * cache reuses those blocks (one more reference each; *n_hit = its length);
+ * every later block is fresh and is entered in the cache under its hash.
+ * PA_ERR_NOSPACE (and no change) if the fresh blocks are not available.
+ *   hashes [n] uint64, ids [n] int32 (written), n_hit (written); host
+ */
+int pa_pool_map_prefix(pa_block_pool* pool, const uint64_t* hashes, int32_t n,
+                       int32_t* ids, int32_t* n_hit);
 
 /* Static text for a status code; never NULL. */
 const char* pa_strerror(int status);

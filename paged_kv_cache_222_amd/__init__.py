@@ -10,13 +10,23 @@ from ._binding import (  # noqa: F401
     PA_BF16,
     PA_F16,
     PA_F32,
+    BlockPool,
     PaError,
     load,
+    pa_block_hashes,
     pa_cache_write,
     pa_copy_blocks,
     pa_decode,
     pa_decode_multi,
     pa_decode_partitioned,
+    pa_pool_alloc,
+    pa_pool_available,
+    pa_pool_create,
+    pa_pool_destroy,
+    pa_pool_fork,
+    pa_pool_map_prefix,
+    pa_pool_refcount,
+    pa_pool_release,
     pa_reduce,
     pa_strerror,
     partition_workspace,

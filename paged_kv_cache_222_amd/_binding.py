@@ -21,6 +21,12 @@ _lib = None
 _lock = threading.Lock()
 
 
+# status codes of include/pa.h
+PA_OK, PA_ERR_NULL, PA_ERR_SHAPE, PA_ERR_UNSUPPORTED = 0, -1, -2, -3
+PA_ERR_WORKSPACE, PA_ERR_PARTITION, PA_ERR_HIP, PA_ERR_ALIGN = -4, -5, -6, -7
+PA_ERR_NOSPACE = -8
+
+
 class PaError(RuntimeError):
     """A non-zero status returned by libpa."""
 
@@ -69,6 +75,27 @@ def load() -> ctypes.CDLL:
         for fn in ("pa_cache_write", "pa_copy_blocks", "pa_decode",
                    "pa_decode_partitioned", "pa_decode_multi", "pa_reduce"):
             getattr(lib, fn).restype = ctypes.c_int
+        u64p = ctypes.POINTER(ctypes.c_uint64)
+        i32p = ctypes.POINTER(ctypes.c_int32)
+        lib.pa_block_hashes.argtypes = [i32p, i32, i32, ctypes.c_uint64, u64p,
+                                        i32p]
+        lib.pa_block_hashes.restype = ctypes.c_int
+        lib.pa_pool_create.argtypes = [i32]
+        lib.pa_pool_create.restype = vp
+        lib.pa_pool_destroy.argtypes = [vp]
+        lib.pa_pool_destroy.restype = None
+        lib.pa_pool_available.argtypes = [vp]
+        lib.pa_pool_available.restype = ctypes.c_int32
+        lib.pa_pool_refcount.argtypes = [vp, i32]
+        lib.pa_pool_refcount.restype = ctypes.c_int32
+        for fn in ("pa_pool_alloc",):
+            getattr(lib, fn).argtypes = [vp, i32, i32p]
+            getattr(lib, fn).restype = ctypes.c_int
+        for fn in ("pa_pool_fork", "pa_pool_release"):
+            getattr(lib, fn).argtypes = [vp, i32p, i32]
+            getattr(lib, fn).restype = ctypes.c_int
+        lib.pa_pool_map_prefix.argtypes = [vp, u64p, i32, i32p, i32p]
+        lib.pa_pool_map_prefix.restype = ctypes.c_int
         lib.pa_strerror.argtypes = [ctypes.c_int]
         lib.pa_strerror.restype = ctypes.c_char_p
         _lib = lib
@@ -302,3 +329,97 @@ def partition_workspace(batch: int, n_q_heads: int, d_head: int,
     to = torch.empty((batch, n_q_heads, max_partitions, d_head),
                      dtype=torch.float32, device=device)
     return ml, es, to
+
+
+# ---------------------------------------------------------------------------
+# host-side block pool and prefix cache (host memory, no GPU)
+# ---------------------------------------------------------------------------
+
+def _i32p(a):
+    return a.ctypes.data_as(ctypes.POINTER(ctypes.c_int32))
+
+
+def pa_block_hashes(tokens, block_size: int, parent: int = 0):
+    """Chained FNV-1a hashes of the full blocks of ``tokens`` (int32);
+    returns a uint64 array of len(tokens) // block_size."""
+    import numpy as np
+    lib = load()
+    t = np.ascontiguousarray(tokens, dtype=np.int32)
+    out = np.zeros(max(1, len(t) // max(1, block_size)), dtype=np.uint64)
+    nf = ctypes.c_int32(0)
+    _check("pa_block_hashes", lib.pa_block_hashes(
+        _i32p(t), len(t), int(block_size), ctypes.c_uint64(parent),
+        out.ctypes.data_as(ctypes.POINTER(ctypes.c_uint64)), ctypes.byref(nf)))
+    return out[:nf.value]
+
+
+class BlockPool:
+    """Owner of a native pa_block_pool (destroyed with this object)."""
+
+    def __init__(self, n_blocks: int):
+        self._lib = load()
+        self.handle = self._lib.pa_pool_create(int(n_blocks))
+        if not self.handle:
+            raise PaError("pa_pool_create", PA_ERR_SHAPE,
+                          "no pool (n_blocks < 1 or out of host memory)")
+        self.n_blocks = int(n_blocks)
+
+    def __del__(self):
+        h = getattr(self, "handle", None)
+        if h:
+            self._lib.pa_pool_destroy(h)
+            self.handle = None
+
+
+def pa_pool_create(n_blocks: int) -> BlockPool:
+    return BlockPool(n_blocks)
+
+
+def pa_pool_destroy(pool: BlockPool) -> None:
+    """Free the native pool now (otherwise it goes with the object)."""
+    if pool.handle:
+        pool._lib.pa_pool_destroy(pool.handle)
+        pool.handle = None
+
+
+def pa_pool_available(pool: BlockPool) -> int:
+    return int(pool._lib.pa_pool_available(pool.handle))
+
+
+def pa_pool_refcount(pool: BlockPool, block: int) -> int:
+    return int(pool._lib.pa_pool_refcount(pool.handle, int(block)))
+
+
+def pa_pool_alloc(pool: BlockPool, n: int):
+    """n fresh block ids (int32 array); raises PaError(PA_ERR_NOSPACE)."""
+    import numpy as np
+    ids = np.zeros(max(1, n), dtype=np.int32)
+    _check("pa_pool_alloc", pool._lib.pa_pool_alloc(pool.handle, int(n),
+                                                   _i32p(ids)))
+    return ids[:n]
+
+
+def pa_pool_fork(pool: BlockPool, ids):
+    import numpy as np
+    a = np.ascontiguousarray(ids, dtype=np.int32)
+    _check("pa_pool_fork", pool._lib.pa_pool_fork(pool.handle, _i32p(a),
+                                                 len(a)))
+
+
+def pa_pool_release(pool: BlockPool, ids):
+    import numpy as np
+    a = np.ascontiguousarray(ids, dtype=np.int32)
+    _check("pa_pool_release", pool._lib.pa_pool_release(pool.handle, _i32p(a),
+                                                       len(a)))
+
+
+def pa_pool_map_prefix(pool: BlockPool, hashes):
+    """(ids, n_hit) for a request's full blocks given their chained hashes."""
+    import numpy as np
+    h = np.ascontiguousarray(hashes, dtype=np.uint64)
+    ids = np.zeros(max(1, len(h)), dtype=np.int32)
+    hit = ctypes.c_int32(0)
+    _check("pa_pool_map_prefix", pool._lib.pa_pool_map_prefix(
+        pool.handle, h.ctypes.data_as(ctypes.POINTER(ctypes.c_uint64)),
+        len(h), _i32p(ids), ctypes.byref(hit)))
+    return ids[:len(h)], hit.value

@@ -34,6 +34,9 @@ HIP_FLAGS = [
 ]
 
 
+CXX_FLAGS = ["-O2", "-std=c++17", "-fPIC", "-Wall"]
+
+
 def hipcc() -> str:
     for cand in (os.environ.get("HIPCC"), shutil.which("hipcc"),
                  "/opt/rocm/bin/hipcc"):
@@ -66,6 +69,15 @@ def build(verbose: bool = False, extra_flags=(), out: str = LIB) -> str:
     with concurrent.futures.ThreadPoolExecutor(jobs) as ex:
         objs = list(ex.map(lambda s: _compile(s, cc, list(extra_flags), build_dir),
                            srcs))
+    for src in sorted(glob.glob(os.path.join(CSRC, "*.cpp"))):   # host-only code
+        obj = os.path.join(build_dir, os.path.basename(src)[:-4] + ".o")
+        cmd = ["g++", *CXX_FLAGS, f"-I{INCLUDE}", f"-I{CSRC}", "-c", src, "-o", obj]
+        res = subprocess.run(cmd, capture_output=True, text=True)
+        if res.returncode != 0:
+            raise RuntimeError(f"g++ failed for {src}:\n{' '.join(cmd)}\n"
+                               f"{res.stdout}\n{res.stderr}")
+        objs.append(obj)
+        srcs.append(src)
     tmp = out + ".tmp"
     cmd = [cc, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp, *objs]
     res = subprocess.run(cmd, capture_output=True, text=True)

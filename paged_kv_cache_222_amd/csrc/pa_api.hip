@@ -191,6 +191,7 @@ const char* pa_strerror(int status) {
     case PA_ERR_PARTITION: return "partition_size must be a positive multiple of block_size";
     case PA_ERR_HIP: return "the HIP runtime reported an error at kernel launch";
     case PA_ERR_ALIGN: return "an array pointer is not 16-byte aligned";
+    case PA_ERR_NOSPACE: return "the block pool has too few free blocks";
     default: return "unknown status";
   }
 }

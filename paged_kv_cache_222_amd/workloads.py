@@ -451,3 +451,23 @@ def multi_token_slots(w: Workload, n_queries: int) -> np.ndarray:
                 out[b, j] = int(w.block_table[b, pos // c.block_size]) * \
                     c.block_size + pos % c.block_size
     return out.reshape(-1).astype(np.int32)
+
+
+# The "Serving" §23.4 widget: a 96-block pool of 16-token blocks and eight
+# requests arriving over time.  The page gives no sizes; these are chosen so
+# that its two statements can be checked: a worst case of 384 tokens (24
+# blocks, so four reservations fill the pool) and final lengths of at most
+# 192 tokens (12 blocks, so eight paged requests fit together).
+WIDGET = dict(n_blocks=96, block_size=16, n_requests=8, max_len=384,
+              arrival_gap=8, prompt=(16, 64), final=(96, 192))
+
+
+def widget_requests(seed: int = 0):
+    """(arrivals, prompt_lens, final_lens) of the widget's eight requests."""
+    w = WIDGET
+    rng = np.random.default_rng(np.random.SeedSequence(seed).spawn(9)[8])
+    n = w["n_requests"]
+    arrivals = [i * w["arrival_gap"] for i in range(n)]
+    prompts = [int(x) for x in rng.integers(w["prompt"][0], w["prompt"][1] + 1, n)]
+    finals = [int(x) for x in rng.integers(w["final"][0], w["final"][1] + 1, n)]
+    return arrivals, prompts, finals

@@ -15,6 +15,7 @@ HEADER = os.path.join(ROOT, "include", "pa.h")
 
 PA_OK, PA_ERR_NULL, PA_ERR_SHAPE, PA_ERR_UNSUPPORTED = 0, -1, -2, -3
 PA_ERR_WORKSPACE, PA_ERR_PARTITION, PA_ERR_HIP, PA_ERR_ALIGN = -4, -5, -6, -7
+PA_ERR_NOSPACE = -8
 
 P = 0x100000        # a fake, 16-byte aligned device address (never touched)
 MIS = P + 8         # misaligned
@@ -28,8 +29,11 @@ def declared_functions():
 
 def test_header_declares_the_entry_points():
     assert declared_functions() == sorted(
-        ["pa_cache_write", "pa_copy_blocks", "pa_decode", "pa_decode_multi",
-         "pa_decode_partitioned", "pa_reduce", "pa_strerror"])
+        ["pa_block_hashes", "pa_cache_write", "pa_copy_blocks", "pa_decode",
+         "pa_decode_multi", "pa_decode_partitioned", "pa_pool_alloc",
+         "pa_pool_available", "pa_pool_create", "pa_pool_destroy",
+         "pa_pool_fork", "pa_pool_map_prefix", "pa_pool_refcount",
+         "pa_pool_release", "pa_reduce", "pa_strerror"])
 
 
 def test_library_exports_every_declared_symbol(lib):
@@ -46,11 +50,12 @@ def test_library_exports_every_declared_symbol(lib):
 def test_strerror_covers_every_status(lib):
     seen = set()
     for st in (PA_OK, PA_ERR_NULL, PA_ERR_SHAPE, PA_ERR_UNSUPPORTED,
-               PA_ERR_WORKSPACE, PA_ERR_PARTITION, PA_ERR_HIP, PA_ERR_ALIGN):
+               PA_ERR_WORKSPACE, PA_ERR_PARTITION, PA_ERR_HIP, PA_ERR_ALIGN,
+               PA_ERR_NOSPACE):
         text = lib.pa_strerror(st).decode()
         assert text and text != "unknown status"
         seen.add(text)
-    assert len(seen) == 8
+    assert len(seen) == 9
     assert lib.pa_strerror(12345).decode() == "unknown status"
 
 
