@@ -8,6 +8,13 @@
 #include "pa_device.h"
 #include "pa_launch.h"
 
+#ifndef PA_COPY_NT_STORE
+#define PA_COPY_NT_STORE 0
+#endif
+#ifndef PA_COPY_NT_LOAD
+#define PA_COPY_NT_LOAD 1
+#endif
+
 namespace pa {
 
 // Work group x copies chunk x % cpb of pool (x / cpb) % 2 of pair
@@ -33,12 +40,24 @@ __global__ __launch_bounds__(kCopyThreads) void copy_blocks_kernel(CopyBlocksArg
 #pragma unroll
   for (int u = 0; u < kCopyUnroll; ++u) {
     const int64_t i = threadIdx.x + u * kCopyThreads;
-    if (i < n16) r[u] = __builtin_nontemporal_load(from + i);
+    if (i < n16) {
+#if PA_COPY_NT_LOAD
+      r[u] = __builtin_nontemporal_load(from + i);
+#else
+      r[u] = from[i];
+#endif
+    }
   }
 #pragma unroll
   for (int u = 0; u < kCopyUnroll; ++u) {
     const int64_t i = threadIdx.x + u * kCopyThreads;
-    if (i < n16) __builtin_nontemporal_store(r[u], to + i);
+    if (i < n16) {
+#if PA_COPY_NT_STORE
+      __builtin_nontemporal_store(r[u], to + i);
+#else
+      to[i] = r[u];
+#endif
+    }
   }
 }
 

@@ -62,7 +62,10 @@ struct CacheWriteArgs {
 };
 
 constexpr int kCopyThreads = 256;
-constexpr int kCopyUnroll = 4;  // 16-byte loads in flight per thread
+#ifndef PA_COPY_UNROLL
+#define PA_COPY_UNROLL 4
+#endif
+constexpr int kCopyUnroll = PA_COPY_UNROLL;  // 16-byte loads in flight per thread
 constexpr int64_t kCopyChunk = (int64_t)kCopyThreads * 16 * kCopyUnroll;  // bytes per work group
 
 struct CopyBlocksArgs {

@@ -10,6 +10,66 @@
 
 namespace pa {
 
+// Workspaces of at most kFewParts partitions: every load of the row (its
+// context length, all m_p, l_p and this lane's o_p elements) is issued at
+// once, then the partitions past the sequence's end are masked, so the row
+// costs one memory round trip instead of three.
+constexpr int kFewParts = 8;
+
+template <Dt DT, int D>
+__global__ __launch_bounds__(kWave) void reduce_few_kernel(ReduceArgs a) {
+  constexpr int DPL = D / kWave;
+  const int lane = threadIdx.x;
+  const int bh = blockIdx.x;
+  const int b = bh / a.n_q_heads;
+  const int PM = a.max_partitions;  // <= kFewParts
+  const float* ml = a.max_logits + (int64_t)bh * PM;
+  const float* es = a.exp_sums + (int64_t)bh * PM;
+  const float* to = a.tmp_out + (int64_t)bh * PM * D + lane * DPL;
+  const int ctx = a.context_lens[b];
+  float m[kFewParts], l[kFewParts], o[kFewParts][DPL];
+#pragma unroll
+  for (int p = 0; p < kFewParts; ++p) {
+    if (p < PM) {
+      m[p] = ml[p];
+      l[p] = es[p];
+#pragma unroll
+      for (int k = 0; k < DPL; ++k) o[p][k] = to[(int64_t)p * D + k];
+    }
+  }
+  const int64_t orow = (int64_t)bh * D;
+  const int P = a.partition_size;
+  const int64_t np64 = ctx > 0 ? ((int64_t)ctx + P - 1) / P : 0;
+  if (ctx < 0 || np64 > PM || np64 == 0) {
+    const float v = (np64 == 0 && ctx == 0) ? 0.0f : __builtin_nanf("");
+#pragma unroll
+    for (int k = 0; k < DPL; ++k) store_elem<DT>(a.out, orow + lane * DPL + k, v);
+    return;
+  }
+  const int np = (int)np64;
+  float M = -__builtin_huge_valf();
+#pragma unroll
+  for (int p = 0; p < kFewParts; ++p)
+    if (p < np) M = fmaxf(M, m[p]);
+  float W = 0.0f, acc[DPL];
+#pragma unroll
+  for (int k = 0; k < DPL; ++k) acc[k] = 0.0f;
+#pragma unroll
+  for (int p = 0; p < kFewParts; ++p) {
+    if (p < np) {
+      const float w = l[p] * exp2_fast((m[p] - M) * kLog2e);
+      W += w;
+#pragma unroll
+      for (int k = 0; k < DPL; ++k) acc[k] = __builtin_fmaf(w, o[p][k], acc[k]);
+    }
+  }
+  // W = 0: a query token that sees no position (multi-token queries only);
+  // a NaN W (a partition flagged bad) stays NaN
+#pragma unroll
+  for (int k = 0; k < DPL; ++k)
+    store_elem<DT>(a.out, orow + lane * DPL + k, W == 0.0f ? 0.0f : acc[k] / W);
+}
+
 template <Dt DT, int D>
 __global__ __launch_bounds__(kWave) void reduce_kernel(ReduceArgs a) {
   constexpr int DPL = D / kWave;  // output elements per lane
@@ -81,12 +141,20 @@ __global__ __launch_bounds__(kWave) void reduce_kernel(ReduceArgs a) {
 template <Dt DT>
 static hipError_t launch_reduce_dt(const ReduceArgs& a, int d_head, hipStream_t s) {
   const unsigned grid = (unsigned)(a.batch * a.n_q_heads);
-  if (d_head == 64)
-    hipLaunchKernelGGL((reduce_kernel<DT, 64>), dim3(grid), dim3(kWave), 0, s, a);
-  else if (d_head == 128)
-    hipLaunchKernelGGL((reduce_kernel<DT, 128>), dim3(grid), dim3(kWave), 0, s, a);
-  else
+  const bool few = a.max_partitions <= kFewParts;
+  if (d_head == 64) {
+    if (few)
+      hipLaunchKernelGGL((reduce_few_kernel<DT, 64>), dim3(grid), dim3(kWave), 0, s, a);
+    else
+      hipLaunchKernelGGL((reduce_kernel<DT, 64>), dim3(grid), dim3(kWave), 0, s, a);
+  } else if (d_head == 128) {
+    if (few)
+      hipLaunchKernelGGL((reduce_few_kernel<DT, 128>), dim3(grid), dim3(kWave), 0, s, a);
+    else
+      hipLaunchKernelGGL((reduce_kernel<DT, 128>), dim3(grid), dim3(kWave), 0, s, a);
+  } else {
     return hipErrorInvalidValue;
+  }
   return hipGetLastError();
 }
 
