@@ -1,9 +1,11 @@
 """Throughput of one paged-attention decode step on one MI355X.
 
-A step is the whole hot path over one batch: pa_cache_write of each
-sequence's new token, then attention over every sequence's paged cache
-(pa_decode_partitioned + pa_reduce, or the single-pass pa_decode; both are
-timed and the faster is reported, with its name).  Inputs are seeded
+A step is the whole hot path over one batch: the cache write of each
+sequence's new token, then attention over every sequence's paged cache.
+Three forms are timed and the fastest is reported, with its name: "fused"
+(pa_decode_step -- the write folded into the partitioned attention -- then
+pa_reduce), "partitioned" (pa_cache_write, pa_decode_partitioned,
+pa_reduce) and "single" (pa_cache_write, the single-pass pa_decode).  Inputs are seeded
 synthetic batches (see paged_kv_cache_222_amd/workloads.py); the default is
 the LLaMA-3-8B-shaped GQA batch (B=128, 32/8 heads, d128, bf16, log-normal
 context lengths).  Several copies of the inputs are resident in HBM and the
@@ -48,7 +50,8 @@ def parse():
     ap.add_argument("--partition-size", type=int, default=None)
     ap.add_argument("--copies", type=int, default=3,
                     help="resident input copies the steps rotate over")
-    ap.add_argument("--variant", choices=["best", "partitioned", "single"],
+    ap.add_argument("--variant", choices=["best", "fused", "partitioned",
+                                          "single"],
                     default="best")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
@@ -513,6 +516,18 @@ def main():
     def step(x, variant, ev=None):
         if ev is not None:
             ev[0].record(stream)
+        if variant == "fused":
+            # the cache write happens inside the attention launch
+            if ev is not None:
+                ev[1].record(stream)
+            pa.pa_decode_step(*ws, x["kn"], x["vn"], x["q"], x["k"], x["v"],
+                              tbl, cl, partition_size=P, scale=w.scale)
+            if ev is not None:
+                ev[2].record(stream)
+            pa.pa_reduce(out, *ws, cl, partition_size=P)
+            if ev is not None:
+                ev[3].record(stream)
+            return
         pa.pa_cache_write(x["kn"], x["vn"], x["k"], x["v"], slots)
         if ev is not None:
             ev[1].record(stream)
@@ -550,7 +565,7 @@ def main():
                         for e in evs]) * 1e3   # microseconds
         return wall, per
 
-    variants = (["partitioned", "single"] if args.variant == "best"
+    variants = (["fused", "partitioned", "single"] if args.variant == "best"
                 else [args.variant])
     results = {}
     for v in variants:
@@ -570,9 +585,13 @@ def main():
     alg = algorithmic_bytes(w)
     if c.prefix_len:
         alg = alg - kv + uniq
+    if best == "fused":   # the new rows are read and written by the same launch
+        alg += 2 * 2 * c.batch * c.n_kv_heads * c.d_head * \
+            {"f32": 4, "f16": 2, "bf16": 2}[c.dtype]
     achieved = alg / (attn_us * 1e-6) / 1e9
-    kernel = ("attention_kernel (pa_decode_partitioned)" if best ==
-              "partitioned" else "attention_kernel (pa_decode)")
+    kernel = {"fused": "attention_mfma_kernel (pa_decode_step)",
+              "partitioned": "attention_mfma_kernel (pa_decode_partitioned)",
+              "single": "attention_mfma_kernel (pa_decode)"}[best]
     rec = {
         "metric": METRIC,
         "value": round(gbs, 2),

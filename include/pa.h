@@ -166,6 +166,32 @@ int pa_decode_partitioned(float* max_logits, float* exp_sums, float* tmp_out,
                           float scale, int32_t dtype, void* stream);
 
 /*
+ * pa_decode_step -- a whole decode step for the partitioned path: the cache
+ * write of each sequence's new token folded into pa_decode_partitioned.
+ * For every sequence with n = context_lens[b] >= 1 whose table entry for
+ * position n - 1 lies in the pool, key_new[b] / value_new[b] are stored at
+ * position n - 1 (block block_table[b][(n-1) / block_size], offset
+ * (n-1) % block_size), every KV head, as a bit copy; then the attention and
+ * the workspace are exactly those of pa_decode_partitioned over the written
+ * cache (pa_reduce finishes).  The result equals pa_cache_write with the
+ * slots of positions n - 1 followed by pa_decode_partitioned, bit for bit,
+ * in one launch: the work item that covers position n - 1 writes the row
+ * and uses it directly.  fp32 runs the write as a separate kernel first.
+ *
+ *   key_new, value_new [batch, n_kv_heads, d_head] dtype, read
+ *   k_pool, v_pool     written at position n - 1 of each sequence, read
+ *   Other arguments as in pa_decode_partitioned.
+ */
+int pa_decode_step(float* max_logits, float* exp_sums, float* tmp_out,
+                   int32_t partition_size, int32_t max_partitions,
+                   const void* key_new, const void* value_new, const void* q,
+                   void* k_pool, void* v_pool, const int32_t* block_table,
+                   int32_t max_blocks, const int32_t* context_lens,
+                   int32_t batch, int32_t n_kv_heads, int32_t gqa_group,
+                   int32_t d_head, int32_t block_size, int32_t n_blocks,
+                   float scale, int32_t dtype, void* stream);
+
+/*
  * pa_decode_multi -- several query tokens per sequence: the last n_queries
  * positions of each sequence, causal among themselves, as in the one pass
  * in which the target model checks all drafted tokens of speculative

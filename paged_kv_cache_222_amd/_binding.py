@@ -65,6 +65,9 @@ def load() -> ctypes.CDLL:
         lib.pa_decode_multi.argtypes = [vp, vp, vp, i32, i32, vp, vp, vp, vp,
                                         i32, vp, i32, i32, i32, i32, i32, i32,
                                         i32, f32, i32, vp]
+        lib.pa_decode_step.argtypes = [vp, vp, vp, i32, i32, vp, vp, vp, vp,
+                                       vp, vp, i32, vp, i32, i32, i32, i32,
+                                       i32, i32, f32, i32, vp]
         lib.pa_decode.argtypes = [vp, vp, vp, vp, vp, i32, vp, i32, i32, i32,
                                   i32, i32, i32, f32, i32, vp]
         lib.pa_decode_partitioned.argtypes = [vp, vp, vp, i32, i32, vp, vp, vp,
@@ -73,7 +76,8 @@ def load() -> ctypes.CDLL:
         lib.pa_reduce.argtypes = [vp, vp, vp, vp, vp, i32, i32, i32, i32, i32,
                                   i32, vp]
         for fn in ("pa_cache_write", "pa_copy_blocks", "pa_decode",
-                   "pa_decode_partitioned", "pa_decode_multi", "pa_reduce"):
+                   "pa_decode_partitioned", "pa_decode_multi", "pa_decode_step",
+                   "pa_reduce"):
             getattr(lib, fn).restype = ctypes.c_int
         u64p = ctypes.POINTER(ctypes.c_uint64)
         i32p = ctypes.POINTER(ctypes.c_int32)
@@ -261,6 +265,37 @@ def pa_decode_partitioned(max_logits, exp_sums, tmp_out, q, k_pool, v_pool,
         v_pool.data_ptr(), block_table.data_ptr(), mb, context_lens.data_ptr(),
         B, n_kv, G, d, bs, n_blocks, float(scale), _dtype_code(q),
         _stream(stream)))
+
+
+def pa_decode_step(max_logits, exp_sums, tmp_out, key_new, value_new, q,
+                   k_pool, v_pool, block_table, context_lens, *, partition_size,
+                   scale, stream=None):
+    """pa_cache_write of each sequence's new token at position
+    context_lens[b] - 1 folded into pa_decode_partitioned (one launch);
+    key_new/value_new [B, n_kv_heads, d_head]."""
+    torch = _torch()
+    lib = load()
+    B, Hq, n_kv, G, d, bs, n_blocks, mb = _attention_common(
+        q, k_pool, v_pool, block_table, context_lens)
+    _dev("key_new", key_new, q.dtype, 3)
+    _dev("value_new", value_new, q.dtype, 3)
+    if tuple(key_new.shape) != (B, n_kv, d) or value_new.shape != key_new.shape:
+        raise ValueError("key_new/value_new must be [B, n_kv_heads, d_head]")
+    _dev("max_logits", max_logits, torch.float32, 3)
+    _dev("exp_sums", exp_sums, torch.float32, 3)
+    _dev("tmp_out", tmp_out, torch.float32, 4)
+    pmax = max_logits.shape[2]
+    if (tuple(max_logits.shape) != (B, Hq, pmax)
+            or tuple(exp_sums.shape) != (B, Hq, pmax)
+            or tuple(tmp_out.shape) != (B, Hq, pmax, d)):
+        raise ValueError("workspace shapes must be [B, Hq, PMAX] and "
+                         "[B, Hq, PMAX, D]")
+    _check("pa_decode_step", lib.pa_decode_step(
+        max_logits.data_ptr(), exp_sums.data_ptr(), tmp_out.data_ptr(),
+        int(partition_size), pmax, key_new.data_ptr(), value_new.data_ptr(),
+        q.data_ptr(), k_pool.data_ptr(), v_pool.data_ptr(),
+        block_table.data_ptr(), mb, context_lens.data_ptr(), B, n_kv, G, d, bs,
+        n_blocks, float(scale), _dtype_code(q), _stream(stream)))
 
 
 def pa_decode_multi(max_logits, exp_sums, tmp_out, q, k_pool, v_pool,

@@ -146,10 +146,13 @@ int decode_partitioned(float* max_logits, float* exp_sums, float* tmp_out,
                        int32_t max_blocks, const int32_t* context_lens, int32_t batch,
                        int32_t n_queries, int32_t n_kv_heads, int32_t gqa_group,
                        int32_t d_head, int32_t block_size, int32_t n_blocks, float scale,
-                       int32_t dtype, void* stream) {
+                       int32_t dtype, void* stream, const void* key_new = nullptr,
+                       const void* value_new = nullptr) {
   if (batch < 0 || n_queries < 1) return PA_ERR_SHAPE;
   if (batch == 0) return PA_OK;
   if (!max_logits || !exp_sums || !tmp_out) return PA_ERR_NULL;
+  if ((key_new != nullptr) != (value_new != nullptr)) return PA_ERR_NULL;
+  if (key_new && (!aligned16(key_new) || !aligned16(value_new))) return PA_ERR_ALIGN;
   int st = check_attention(q, k_pool, v_pool, block_table, max_blocks, context_lens, batch,
                            n_kv_heads, gqa_group, d_head, block_size, n_blocks, dtype);
   if (st != PA_OK) return st;
@@ -172,6 +175,29 @@ int decode_partitioned(float* max_logits, float* exp_sums, float* tmp_out,
   if (rows * n_kv_heads * (((int64_t)gqa_group * n_queries + 7) / 8) > INT_MAX)
     return PA_ERR_SHAPE;
   (void)hipGetLastError();
+  if (key_new) {
+    if (dtype == PA_F32) {
+      // no folded write on the vector-ALU kernel: a separate append first
+      pa::AppendArgs w{};
+      w.key = key_new;
+      w.value = value_new;
+      w.k_pool = const_cast<void*>(k_pool);
+      w.v_pool = const_cast<void*>(v_pool);
+      w.block_table = block_table;
+      w.context_lens = context_lens;
+      w.batch = batch;
+      w.max_blocks = max_blocks;
+      w.n_kv_heads = n_kv_heads;
+      w.row_bytes = d_head * elem_bytes(dtype);
+      w.block_shift = block_shift_of(block_size);
+      w.n_blocks = n_blocks;
+      const hipError_t e = pa::launch_append(w, (hipStream_t)stream);
+      if (e != hipSuccess) return launch_status(e);
+    } else {
+      a.key_new = key_new;
+      a.value_new = value_new;
+    }
+  }
   int st2 = PA_OK;
   const hipError_t e = dispatch_attention(a, dtype, d_head, rows, (hipStream_t)stream, &st2);
   return st2 != PA_OK ? st2 : launch_status(e);
@@ -285,6 +311,19 @@ int pa_decode_partitioned(float* max_logits, float* exp_sums, float* tmp_out,
                             k_pool, v_pool, block_table, max_blocks, context_lens, batch, 1,
                             n_kv_heads, gqa_group, d_head, block_size, n_blocks, scale, dtype,
                             stream);
+}
+
+int pa_decode_step(float* max_logits, float* exp_sums, float* tmp_out, int32_t partition_size,
+                   int32_t max_partitions, const void* key_new, const void* value_new,
+                   const void* q, void* k_pool, void* v_pool, const int32_t* block_table,
+                   int32_t max_blocks, const int32_t* context_lens, int32_t batch,
+                   int32_t n_kv_heads, int32_t gqa_group, int32_t d_head, int32_t block_size,
+                   int32_t n_blocks, float scale, int32_t dtype, void* stream) {
+  if (batch > 0 && (!key_new || !value_new)) return PA_ERR_NULL;
+  return decode_partitioned(max_logits, exp_sums, tmp_out, partition_size, max_partitions, q,
+                            k_pool, v_pool, block_table, max_blocks, context_lens, batch, 1,
+                            n_kv_heads, gqa_group, d_head, block_size, n_blocks, scale, dtype,
+                            stream, key_new, value_new);
 }
 
 int pa_decode_multi(float* max_logits, float* exp_sums, float* tmp_out, int32_t partition_size,

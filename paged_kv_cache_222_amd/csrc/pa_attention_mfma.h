@@ -409,6 +409,21 @@ __global__ __launch_bounds__(kAttnThreads, PA_MFMA_MIN_BLOCKS) void attention_mf
     t0 = __builtin_amdgcn_readfirstlane(t0);
     t1 = __builtin_amdgcn_readfirstlane(t1);
     const int ntile = (t1 - t0 + 15) >> 4;
+    // The folded cache write (decode only): the work item holding position
+    // ctx - 1 -- the sequence's final partition -- stores the new row of its
+    // KV head in the pool, and the wave that owns that position's tile
+    // patches it into the tile in LDS after the tile's copy lands (the copy
+    // may predate the store), so the attention reads the new row either way.
+    const bool append = a.key_new != nullptr && t1 == ctx && ctx > 0;
+    const int tn = ctx - 1;
+    const int ti_new = (tn - t0) >> 4;                     // its tile in the item
+    const int wave_new = ti_new % NW, i_new = ti_new / NW, r_new = (tn - t0) & 15;
+    u32x4 knew = u32x4{0u, 0u, 0u, 0u}, vnew = u32x4{0u, 0u, 0u, 0u};
+    if (append && wave == wave_new && lane < CPR) {
+      const int64_t src = (int64_t)(b * a.n_kv_heads + kvh) * RB + lane * 16;
+      knew = *(const u32x4*)((const char*)a.key_new + src);
+      vnew = *(const u32x4*)((const char*)a.value_new + src);
+    }
     const int lim_min = ctx - NQ + 1;                      // of the first query token
     const int lim_lane = lim_min + (c0 + l16) / G;         // of this lane's column
     const int my_n = __builtin_amdgcn_readfirstlane(ntile > wave ? (ntile - 1 - wave) / NW + 1 : 0);
@@ -487,6 +502,24 @@ __global__ __launch_bounds__(kAttnThreads, PA_MFMA_MIN_BLOCKS) void attention_mf
       k_addr[kk] = ring_lds + l16 * RB + (((kk * 4 + lg) ^ (l16 % CPR)) * 16);
     const uint32_t v_addr = ring_lds + (lg * 4 + (l16 >> 2)) * RB + (l16 & 3) * 8;
 
+    // After tile i's copy has landed: the folded cache write (see above).
+    auto patch_new_row = [&](int i, int slot) {
+      if (!append || wave != wave_new || i != i_new) return;
+      const int pblk = trow[tn >> a.block_shift];
+      if (lane < CPR) {
+        char* kd = my_ring + (2 * slot) * TILE;
+        *(u32x4*)(kd + r_new * RB + ((lane ^ (r_new % CPR)) * 16)) = knew;
+        *(u32x4*)(kd + TILE + r_new * RB + lane * 16) = vnew;
+        if (pblk >= 0 && pblk < a.n_blocks) {
+          const int64_t dst = (int64_t)pblk * blk_bytes + (int64_t)(tn & (bs - 1)) * RB + lane * 16;
+          *(u32x4*)((char*)kbase + dst) = knew;
+          *(u32x4*)((char*)vbase + dst) = vnew;
+        }
+      }
+      __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0): the LDS stores are done
+      asm volatile("" ::: "memory");       // and ordered before the tile's reads
+    };
+
     auto compute = [&](int i, auto slot_tag) {
       constexpr int SLOT = decltype(slot_tag)::value;
       const int tok = __builtin_amdgcn_readfirstlane(t0 + (wave + i * NW) * 16);
@@ -564,6 +597,7 @@ __global__ __launch_bounds__(kAttnThreads, PA_MFMA_MIN_BLOCKS) void attention_mf
         } else {
           __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
         }
+        patch_new_row(i, 0);
         compute(i, std::integral_constant<int, 0>{});
         if (i + 1 >= my_n) break;
         if (i + 2 < my_n) {
@@ -572,6 +606,7 @@ __global__ __launch_bounds__(kAttnThreads, PA_MFMA_MIN_BLOCKS) void attention_mf
         } else {
           __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
         }
+        patch_new_row(i + 1, 1);
         compute(i + 1, std::integral_constant<int, 1>{});
       }
     }

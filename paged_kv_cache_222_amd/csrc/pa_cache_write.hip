@@ -35,6 +35,38 @@ __global__ __launch_bounds__(kWriteThreads) void cache_write_kernel(CacheWriteAr
   *(u32x4*)((char*)a.v_pool + dst) = vv;
 }
 
+// The same copy with the slot taken from the block table: each sequence's
+// new row goes to position context_lens[b] - 1 (a sequence with no position
+// or whose table entry lies outside the pool is skipped).
+__global__ __launch_bounds__(kWriteThreads) void append_kernel(AppendArgs a) {
+  const int cpr = a.row_bytes >> 4;
+  const int64_t per_seq = (int64_t)a.n_kv_heads * cpr;
+  const int64_t gid = (int64_t)blockIdx.x * kWriteThreads + threadIdx.x;
+  if (gid >= per_seq * a.batch) return;
+  const int b = (int)(gid / per_seq);
+  const int rem = (int)(gid - (int64_t)b * per_seq);
+  const int h = rem / cpr;
+  const int c = rem - h * cpr;
+  const int ctx = a.context_lens[b];
+  if (ctx < 1 || (int64_t)ctx > ((int64_t)a.max_blocks << a.block_shift)) return;
+  const int pos = ctx - 1;
+  const int blk = a.block_table[(int64_t)b * a.max_blocks + (pos >> a.block_shift)];
+  if (blk < 0 || blk >= a.n_blocks) return;
+  const int off = pos & ((1 << a.block_shift) - 1);
+  const int64_t dst = ((((int64_t)blk * a.n_kv_heads + h) << a.block_shift) + off) * a.row_bytes + c * 16;
+  const u32x4 kv = *(const u32x4*)((const char*)a.key + gid * 16);
+  const u32x4 vv = *(const u32x4*)((const char*)a.value + gid * 16);
+  *(u32x4*)((char*)a.k_pool + dst) = kv;
+  *(u32x4*)((char*)a.v_pool + dst) = vv;
+}
+
+hipError_t launch_append(const AppendArgs& a, hipStream_t s) {
+  const int64_t chunks = (int64_t)a.batch * a.n_kv_heads * (a.row_bytes >> 4);
+  const unsigned grid = (unsigned)((chunks + kWriteThreads - 1) / kWriteThreads);
+  hipLaunchKernelGGL(append_kernel, dim3(grid), dim3(kWriteThreads), 0, s, a);
+  return hipGetLastError();
+}
+
 hipError_t launch_cache_write(const CacheWriteArgs& a, hipStream_t s) {
   const int64_t chunks = (int64_t)a.n_tokens * a.n_kv_heads * (a.row_bytes >> 4);
   const unsigned grid = (unsigned)((chunks + kWriteThreads - 1) / kWriteThreads);

@@ -21,6 +21,11 @@ struct AttnArgs {
   float* max_logits;
   float* exp_sums;
   float* tmp_out;
+  // Partitioned decode with the step's cache write folded in: each
+  // sequence's new key/value row [n_kv_heads, d_head] goes to position
+  // context_len - 1 (null: no write).
+  const void* key_new;
+  const void* value_new;
   int32_t max_blocks;
   int32_t batch;
   int32_t n_kv_heads;
@@ -61,6 +66,21 @@ struct CacheWriteArgs {
   int32_t n_blocks;
 };
 
+struct AppendArgs {
+  const void* key;      // [batch, n_kv_heads, d_head]
+  const void* value;
+  void* k_pool;
+  void* v_pool;
+  const int32_t* block_table;
+  const int32_t* context_lens;
+  int32_t batch;
+  int32_t max_blocks;
+  int32_t n_kv_heads;
+  int32_t row_bytes;
+  int32_t block_shift;
+  int32_t n_blocks;
+};
+
 constexpr int kCopyThreads = 256;
 #ifndef PA_COPY_UNROLL
 #define PA_COPY_UNROLL 4
@@ -88,6 +108,7 @@ hipError_t launch_attention_mfma_bf16(const AttnArgs& a, int d_head, unsigned gr
 int attention_mfma_occupancy(int dtype, int d_head);
 hipError_t launch_reduce(const ReduceArgs& a, int dtype, int d_head, hipStream_t s);
 hipError_t launch_cache_write(const CacheWriteArgs& a, hipStream_t s);
+hipError_t launch_append(const AppendArgs& a, hipStream_t s);
 hipError_t launch_copy_blocks(const CopyBlocksArgs& a, hipStream_t s);
 
 constexpr int kAttnThreads = 256;  // four waves per work item
