@@ -5,31 +5,35 @@
 // ("Serving" section 23.2: decode reads the whole cached K/V of a sequence for
 // one query token; section 23.4: fixed-size blocks and a per-sequence table).
 // The G query heads that share a KV head (section 23.1) are one work item, so
-// each K/V byte is read from HBM once per step.
+// each K/V byte is read from HBM once per step.  With n_queries > 1 the
+// columns of a work item are (query token, head) pairs of the last
+// n_queries positions, causal among themselves (the verify pass of
+// speculative decoding, section 23.5), still one read of each K/V byte.
 //
 // Tiles of 16 consecutive positions.  For a tile:
 //   S = K Q^T       v_mfma_f32_16x16x32: A = K rows (lane l: position l%16,
-//                   16 bytes at dims 32j + 8(l/16)), loaded straight from HBM;
-//                   B = the queries (lane l: head l%16, zero past the group);
-//                   C = S (lane l: positions 4(l/16)+i, head l%16)
+//                   16 bytes at dims 32j + 8(l/16)); B = the queries (lane l:
+//                   column l%16, zero past the chunk); C = S (lane l:
+//                   positions 4(l/16)+i, column l%16)
 //   P = exp2(S*scale*log2e - m), rounded to the storage type
 //   O += P V        v_mfma_f32_16x16x16: A = P, which is exactly the C layout
-//                   of S; B = V (lane l: positions 4(l/16)..+3 of dim l%16) —
-//                   V rows are copied HBM -> LDS with global_load_lds and read
-//                   back transposed with ds_read_b64_tr_b16.
-// The running maximum m is per head and shared by the four lanes holding that
-// head; it is raised only when a tile's maximum exceeds it by more than kTau
+//                   of S; B = V (lane l: positions 4(l/16)..+3 of dim l%16).
+// K and V tiles are copied HBM -> LDS with global_load_lds (non-temporal);
+// K is read back with ds_read_b128 (16-byte chunks swizzled per row against
+// bank conflicts), V transposed with ds_read_b64_tr_b16.
+// The running maximum m is per column and shared by the four lanes holding
+// it; it is raised only when a tile's maximum exceeds it by more than kTau
 // (log2 units), so exp2(S - m) <= 2^kTau.  The normaliser l sums the rounded
 // P, so the weights applied to V are exactly the ones summed.
 //
-// Work items are (sequence, KV head, chunk of <= 16 query heads[, partition])
-// and four waves share one item, taking its tiles round-robin; their states
-// are merged in LDS with the log-sum-exp rule at the end of the item.
-// Partitioned launches are persistent: each work group derives the list of
-// non-empty (sequence, partition) items from the context lengths, ordered
-// full partitions first and each sequence's final partial partition last,
-// and takes every gridDim.x-th item.  No work group is launched for an empty
-// partition.
+// Work items are (sequence, KV head, chunk of <= 16 columns[, partition])
+// and four waves share one item, taking its tiles round-robin, each wave
+// double-buffering its own two slots; their states are merged in LDS with
+// the log-sum-exp rule at the end of the item.  Partitioned launches are
+// persistent: every work group derives the same item list from the context
+// lengths (full partitions, then final partitions longest first) and takes
+// its items in a back-and-forth deal over the work groups of its column.
+// No work group is launched for an empty partition.
 #pragma once
 
 #include <type_traits>

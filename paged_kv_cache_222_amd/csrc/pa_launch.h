@@ -112,7 +112,7 @@ hipError_t launch_append(const AppendArgs& a, hipStream_t s);
 hipError_t launch_copy_blocks(const CopyBlocksArgs& a, hipStream_t s);
 
 constexpr int kAttnThreads = 256;  // four waves per work item
-constexpr int kMfmaHeads = 16;     // query heads per work item on the matrix cores
+constexpr int kMfmaHeads = 16;     // columns (query token, head pairs) per matrix-core work item
 constexpr int kPlanBatch = 1024;   // largest batch the in-kernel partition plan handles
 
 }  // namespace pa
