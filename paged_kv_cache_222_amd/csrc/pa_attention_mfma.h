@@ -147,6 +147,12 @@ struct ReadTile {
   }
 };
 
+// Work-group barrier after this wave's LDS accesses completed; unlike
+// __syncthreads it does not wait for vector-memory operations in flight.
+__device__ __forceinline__ void lds_barrier() {
+  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" : : : "memory");
+}
+
 __device__ __forceinline__ int shfl_xor_i(int x, int m) {
   return __builtin_amdgcn_ds_bpermute((__lane_id() ^ m) << 2, x);
 }
@@ -618,7 +624,10 @@ __global__ __launch_bounds__(kAttnThreads, PA_MFMA_MIN_BLOCKS) void attention_mf
     // ---- merge the waves
     float lh = lsum + shfl_xor_f(lsum, 16);
     lh += shfl_xor_f(lh, 32);
-    __syncthreads();  // every wave is done with its ring
+    // The merge's barriers wait for LDS work only: __syncthreads would also
+    // wait for every vector-memory operation in flight, the previous item's
+    // output stores included.
+    lds_barrier();  // every wave is done with its ring
     if (lane < 16) {
       s_m[wave][lane] = m;
       s_l[wave][lane] = lh;
@@ -632,7 +641,7 @@ __global__ __launch_bounds__(kAttnThreads, PA_MFMA_MIN_BLOCKS) void attention_mf
         for (int n = 0; n < ND; ++n) s_o[(wave * 16 + h) * D + n * 16 + l16] = O[n][j];
       }
     }
-    __syncthreads();
+    lds_barrier();
     bool anybad = false;
 #pragma unroll
     for (int w = 0; w < NW; ++w) anybad |= s_bad[w] != 0;
@@ -662,7 +671,7 @@ __global__ __launch_bounds__(kAttnThreads, PA_MFMA_MIN_BLOCKS) void attention_mf
                        anybad ? qnan : (L > 0.0f ? Ov / L : 0.0f));
       }
     }
-    __syncthreads();  // the merge buffer is the next item's rings
+    lds_barrier();  // the merge buffer is the next item's rings
   }
 }
 
