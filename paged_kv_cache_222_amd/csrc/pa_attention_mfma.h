@@ -645,30 +645,60 @@ __global__ __launch_bounds__(kAttnThreads, PA_MFMA_MIN_BLOCKS) void attention_mf
     bool anybad = false;
 #pragma unroll
     for (int w = 0; w < NW; ++w) anybad |= s_bad[w] != 0;
-    for (int idx = threadIdx.x; idx < gv * D; idx += kAttnThreads) {
-      const int g = idx / D, d = idx - g * D;
+    // Thread (column g, dims d..d+3) of pass j: 4 outputs per thread, so a
+    // 16-column chunk takes NP passes of the work group.  Every LDS read of
+    // the merge comes before its first store: the compiler orders reads of
+    // the rings after all vector-memory operations in flight (the copies
+    // into them), and a read after a store would wait for that store.
+    constexpr int D4 = D / 4;
+    constexpr int NP = (16 * D4 + kAttnThreads - 1) / kAttnThreads;
+    float mw[NP][NW], lw[NP][NW];
+    f32x4_t ow[NP][NW];
+#pragma unroll
+    for (int j = 0; j < NP; ++j) {
+      const int idx = threadIdx.x + j * kAttnThreads;
+      if (idx < gv * D4) {
+        const int g = idx / D4, d = (idx - g * D4) * 4;
+#pragma unroll
+        for (int w = 0; w < NW; ++w) {
+          mw[j][w] = s_m[w][g];
+          lw[j][w] = s_l[w][g];
+          ow[j][w] = *reinterpret_cast<const f32x4_t*>(&s_o[(w * 16 + g) * D + d]);
+        }
+      }
+    }
+#pragma unroll
+    for (int j = 0; j < NP; ++j) {
+      const int idx = threadIdx.x + j * kAttnThreads;
+      if (idx >= gv * D4) break;
+      const int g = idx / D4, d = (idx - g * D4) * 4;
       float M = -__builtin_huge_valf();
 #pragma unroll
-      for (int w = 0; w < NW; ++w) M = fmaxf(M, s_m[w][g]);
-      float L = 0.0f, Ov = 0.0f;
+      for (int w = 0; w < NW; ++w) M = fmaxf(M, mw[j][w]);
+      float L = 0.0f;
+      f32x4_t Ov = f32x4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int w = 0; w < NW; ++w) {
-        const float mw = s_m[w][g];
-        const float aw = exp2_fast(mw - M);  // waves without positions have l = 0
-        L += aw * s_l[w][g];
-        Ov += aw * s_o[(w * 16 + g) * D + d];
+        const float aw = exp2_fast(mw[j][w] - M);  // waves without positions have l = 0
+        L += aw * lw[j][w];
+#pragma unroll
+        for (int k = 0; k < 4; ++k) Ov[k] += aw * ow[j][w][k];
       }
+      // a column with no visible position in the partition: l = 0, o = 0
+      f32x4_t r;
+#pragma unroll
+      for (int k = 0; k < 4; ++k) r[k] = anybad ? qnan : (L > 0.0f ? Ov[k] / L : 0.0f);
       if (parts) {
-        // a column with no visible position in the partition: l = 0, o = 0
         const int64_t prow = row_of(g) * a.max_partitions + p;
-        a.tmp_out[prow * D + d] = anybad ? qnan : (L > 0.0f ? Ov / L : 0.0f);
+        *reinterpret_cast<f32x4_t*>(&a.tmp_out[prow * D + d]) = r;
         if (d == 0) {
           a.max_logits[prow] = anybad ? qnan : M * kLn2;
           a.exp_sums[prow] = anybad ? qnan : L;
         }
       } else {
-        store_elem<DT>(a.out, row_of(g) * D + d,
-                       anybad ? qnan : (L > 0.0f ? Ov / L : 0.0f));
+        const int64_t o = row_of(g) * D + d;
+#pragma unroll
+        for (int k = 0; k < 4; ++k) store_elem<DT>(a.out, o + k, r[k]);
       }
     }
     lds_barrier();  // the merge buffer is the next item's rings
