@@ -52,10 +52,11 @@ def parse():
     ap.add_argument("--copies", type=int, default=3,
                     help="resident input copies the steps rotate over")
     ap.add_argument("--variant", choices=["all", "best", "fused",
-                                          "partitioned", "single"],
+                                          "partitioned", "single", "prefix"],
                     default="all",
                     help="all (default): time every form, report the fused "
-                         "step; best: report the fastest form")
+                         "step (the shared-prefix step for a batch with a "
+                         "shared prefix); best: report the fastest form")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
                     help="budget of the CPU oracle sample")
@@ -519,12 +520,21 @@ def main():
     def step(x, variant, ev=None):
         if ev is not None:
             ev[0].record(stream)
-        if variant == "fused":
+        if variant in ("fused", "prefix"):
             # the cache write happens inside the attention launch
             if ev is not None:
                 ev[1].record(stream)
-            pa.pa_decode_step(*ws, x["kn"], x["vn"], x["q"], x["k"], x["v"],
-                              tbl, cl, partition_size=P, scale=w.scale)
+            if variant == "fused":
+                pa.pa_decode_step(*ws, x["kn"], x["vn"], x["q"], x["k"],
+                                  x["v"], tbl, cl, partition_size=P,
+                                  scale=w.scale)
+            else:
+                # the shared prompt's partitions computed for several
+                # sequences per work item
+                pa.pa_decode_shared_prefix(
+                    *ws, x["q"], x["k"], x["v"], tbl, cl, partition_size=P,
+                    prefix_len=c.prefix_len, scale=w.scale,
+                    key_new=x["kn"], value_new=x["vn"])
             if ev is not None:
                 ev[2].record(stream)
             pa.pa_reduce(out, *ws, cl, partition_size=P)
@@ -570,6 +580,10 @@ def main():
 
     variants = (["fused", "partitioned", "single"]
                 if args.variant in ("all", "best") else [args.variant])
+    if c.prefix_len and args.variant in ("all", "best"):
+        variants.insert(0, "prefix")
+    if args.variant == "prefix" and not c.prefix_len:
+        sys.exit("--variant prefix needs a batch with a shared prefix")
     results = {}
     for v in variants:
         log(f"timing {v}: warmup {args.warmup}, steps {args.steps}")
@@ -578,8 +592,9 @@ def main():
         log(f"{v}: {wall / args.steps * 1e3:.4f} ms/step wall; kernel us "
             f"write {per[:, 0].mean():.1f} attn {per[:, 1].mean():.1f} "
             f"reduce {per[:, 2].mean():.1f}")
+    headline = "prefix" if c.prefix_len else "fused"
     best = (min(results, key=lambda v: results[v][0]) if args.variant == "best"
-            else "fused" if args.variant == "all" else args.variant)
+            else headline if args.variant == "all" else args.variant)
     wall, per = results[best]
     ms = wall / args.steps * 1e3
     kv = w.kv_bytes_logical()
@@ -589,11 +604,12 @@ def main():
     alg = algorithmic_bytes(w)
     if c.prefix_len:
         alg = alg - kv + uniq
-    if best == "fused":   # the new rows are read and written by the same launch
+    if best in ("fused", "prefix"):   # the new rows are read and written by the same launch
         alg += 2 * 2 * c.batch * c.n_kv_heads * c.d_head * \
             {"f32": 4, "f16": 2, "bf16": 2}[c.dtype]
     achieved = alg / (attn_us * 1e-6) / 1e9
     kernel = {"fused": "attention_mfma_kernel (pa_decode_step)",
+              "prefix": "attention_mfma_kernel (pa_decode_shared_prefix)",
               "partitioned": "attention_mfma_kernel (pa_decode_partitioned)",
               "single": "attention_mfma_kernel (pa_decode)"}[best]
     rec = {
@@ -624,7 +640,10 @@ def main():
         "kernel_us": {"cache_write": round(float(per[:, 0].mean()), 2),
                       "attention": round(attn_us, 2),
                       "reduce": round(float(per[:, 2].mean()), 2),
-                      "step_events": round(float(per[:, 3].mean()), 2)},
+                      "step_events": round(float(per[:, 3].mean()), 2),
+                      "step_events_p10_p50_p90": [
+                          round(float(x), 2) for x in
+                          np.percentile(per[:, 3], [10, 50, 90])]},
         "variants_ms_per_step": {v: round(results[v][0] / args.steps * 1e3, 5)
                                  for v in results},
         "roofline": {"kernel": kernel, "bound": "hbm",

@@ -192,6 +192,43 @@ int pa_decode_step(float* max_logits, float* exp_sums, float* tmp_out,
                    float scale, int32_t dtype, void* stream);
 
 /*
+ * pa_decode_shared_prefix -- pa_decode_partitioned (key_new == NULL) or
+ * pa_decode_step (key_new != NULL) for a batch whose sequences share a
+ * prefix, such as a long system prompt, through the same physical blocks
+ * ("Serving", section 23.4: sequences with a common prefix can share its
+ * blocks).  The workspace it writes is the one those calls define, read by
+ * pa_reduce; the values differ from theirs only by rounding order.
+ *
+ * Precondition: positions [0, prefix_len) of every sequence map to the same
+ * physical blocks (the first ceil(prefix_len / block_size) table entries
+ * are equal in every row).  The first floor(prefix_len / partition_size)
+ * partitions -- fewer if some sequence with a valid length (1..max_blocks *
+ * block_size) ends in or before them -- are then computed for several
+ * sequences in one work item: each K/V tile of the prefix is read once for
+ * 16 / gqa_group sequences (at least one) instead of once per sequence.  If
+ * the rows do not share those entries the result is attention over the
+ * first row's prefix blocks for every sequence of the item; out-of-pool
+ * block ids still give NaN, never an out-of-bounds read.  With batch >
+ * 1024, fp32, or a device too small for one work group per KV head the call
+ * is pa_decode_partitioned / pa_decode_step (prefix_len unused).
+ *
+ *   prefix_len >= 0 (PA_ERR_SHAPE otherwise)
+ *   key_new, value_new  both NULL, or both [batch, n_kv_heads, d_head] dtype
+ *                       (one NULL: PA_ERR_NULL); the write of pa_decode_step
+ *   Other arguments as in pa_decode_step.
+ */
+int pa_decode_shared_prefix(float* max_logits, float* exp_sums, float* tmp_out,
+                            int32_t partition_size, int32_t max_partitions,
+                            const void* key_new, const void* value_new,
+                            const void* q, void* k_pool, void* v_pool,
+                            const int32_t* block_table, int32_t max_blocks,
+                            const int32_t* context_lens, int32_t batch,
+                            int32_t n_kv_heads, int32_t gqa_group,
+                            int32_t d_head, int32_t block_size,
+                            int32_t n_blocks, int32_t prefix_len, float scale,
+                            int32_t dtype, void* stream);
+
+/*
  * pa_decode_multi -- several query tokens per sequence: the last n_queries
  * positions of each sequence, causal among themselves, as in the one pass
  * in which the target model checks all drafted tokens of speculative

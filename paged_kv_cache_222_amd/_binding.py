@@ -68,6 +68,10 @@ def load() -> ctypes.CDLL:
         lib.pa_decode_step.argtypes = [vp, vp, vp, i32, i32, vp, vp, vp, vp,
                                        vp, vp, i32, vp, i32, i32, i32, i32,
                                        i32, i32, f32, i32, vp]
+        lib.pa_decode_shared_prefix.argtypes = [vp, vp, vp, i32, i32, vp, vp,
+                                                vp, vp, vp, vp, i32, vp, i32,
+                                                i32, i32, i32, i32, i32, i32,
+                                                f32, i32, vp]
         lib.pa_decode.argtypes = [vp, vp, vp, vp, vp, i32, vp, i32, i32, i32,
                                   i32, i32, i32, f32, i32, vp]
         lib.pa_decode_partitioned.argtypes = [vp, vp, vp, i32, i32, vp, vp, vp,
@@ -77,7 +81,7 @@ def load() -> ctypes.CDLL:
                                   i32, vp]
         for fn in ("pa_cache_write", "pa_copy_blocks", "pa_decode",
                    "pa_decode_partitioned", "pa_decode_multi", "pa_decode_step",
-                   "pa_reduce"):
+                   "pa_decode_shared_prefix", "pa_reduce"):
             getattr(lib, fn).restype = ctypes.c_int
         u64p = ctypes.POINTER(ctypes.c_uint64)
         i32p = ctypes.POINTER(ctypes.c_int32)
@@ -296,6 +300,45 @@ def pa_decode_step(max_logits, exp_sums, tmp_out, key_new, value_new, q,
         q.data_ptr(), k_pool.data_ptr(), v_pool.data_ptr(),
         block_table.data_ptr(), mb, context_lens.data_ptr(), B, n_kv, G, d, bs,
         n_blocks, float(scale), _dtype_code(q), _stream(stream)))
+
+
+def pa_decode_shared_prefix(max_logits, exp_sums, tmp_out, q, k_pool, v_pool,
+                            block_table, context_lens, *, partition_size,
+                            prefix_len, scale, key_new=None, value_new=None,
+                            stream=None):
+    """pa_decode_partitioned (key_new None) or pa_decode_step for a batch
+    whose rows share their first prefix_len positions' blocks: the shared
+    partitions are computed for several sequences per work item."""
+    torch = _torch()
+    lib = load()
+    B, Hq, n_kv, G, d, bs, n_blocks, mb = _attention_common(
+        q, k_pool, v_pool, block_table, context_lens)
+    if (key_new is None) != (value_new is None):
+        raise ValueError("key_new and value_new go together")
+    if key_new is not None:
+        _dev("key_new", key_new, q.dtype, 3)
+        _dev("value_new", value_new, q.dtype, 3)
+        if tuple(key_new.shape) != (B, n_kv, d) or \
+                value_new.shape != key_new.shape:
+            raise ValueError("key_new/value_new must be [B, n_kv_heads, d_head]")
+    _dev("max_logits", max_logits, torch.float32, 3)
+    _dev("exp_sums", exp_sums, torch.float32, 3)
+    _dev("tmp_out", tmp_out, torch.float32, 4)
+    pmax = max_logits.shape[2]
+    if (tuple(max_logits.shape) != (B, Hq, pmax)
+            or tuple(exp_sums.shape) != (B, Hq, pmax)
+            or tuple(tmp_out.shape) != (B, Hq, pmax, d)):
+        raise ValueError("workspace shapes must be [B, Hq, PMAX] and "
+                         "[B, Hq, PMAX, D]")
+    _check("pa_decode_shared_prefix", lib.pa_decode_shared_prefix(
+        max_logits.data_ptr(), exp_sums.data_ptr(), tmp_out.data_ptr(),
+        int(partition_size), pmax,
+        None if key_new is None else key_new.data_ptr(),
+        None if value_new is None else value_new.data_ptr(),
+        q.data_ptr(), k_pool.data_ptr(), v_pool.data_ptr(),
+        block_table.data_ptr(), mb, context_lens.data_ptr(), B, n_kv, G, d, bs,
+        n_blocks, int(prefix_len), float(scale), _dtype_code(q),
+        _stream(stream)))
 
 
 def pa_decode_multi(max_logits, exp_sums, tmp_out, q, k_pool, v_pool,

@@ -131,6 +131,15 @@ hipError_t dispatch_attention(pa::AttnArgs a, int32_t dtype, int32_t d_head, int
     a.persistent = 1;
     grid = std::min(grid, slots - slots % cols);
   }
+  // Shared-prefix items need the in-kernel plan and one query token; without
+  // them every sequence reads its prefix through its own table (the same
+  // attention, rounded in a different order).
+  if (a.prefix_parts > 0 && a.persistent && a.n_queries == 1) {
+    a.prefix_seqs = std::max(1, pa::kMfmaHeads * a.n_hchunks / a.gqa_group);
+  } else {
+    a.prefix_parts = 0;
+    a.prefix_seqs = 0;
+  }
   if (grid > INT_MAX || cols > INT_MAX) {
     *status = PA_ERR_SHAPE;
     return hipSuccess;
@@ -147,7 +156,7 @@ int decode_partitioned(float* max_logits, float* exp_sums, float* tmp_out,
                        int32_t n_queries, int32_t n_kv_heads, int32_t gqa_group,
                        int32_t d_head, int32_t block_size, int32_t n_blocks, float scale,
                        int32_t dtype, void* stream, const void* key_new = nullptr,
-                       const void* value_new = nullptr) {
+                       const void* value_new = nullptr, int32_t prefix_len = 0) {
   if (batch < 0 || n_queries < 1) return PA_ERR_SHAPE;
   if (batch == 0) return PA_OK;
   if (!max_logits || !exp_sums || !tmp_out) return PA_ERR_NULL;
@@ -171,6 +180,8 @@ int decode_partitioned(float* max_logits, float* exp_sums, float* tmp_out,
   a.partition_size = partition_size;
   a.max_partitions = max_partitions;
   a.n_queries = n_queries;
+  if (prefix_len < 0) return PA_ERR_SHAPE;
+  a.prefix_parts = prefix_len / partition_size;
   const int64_t rows = (int64_t)max_partitions * batch;
   if (rows * n_kv_heads * (((int64_t)gqa_group * n_queries + 7) / 8) > INT_MAX)
     return PA_ERR_SHAPE;
@@ -324,6 +335,20 @@ int pa_decode_step(float* max_logits, float* exp_sums, float* tmp_out, int32_t p
                             k_pool, v_pool, block_table, max_blocks, context_lens, batch, 1,
                             n_kv_heads, gqa_group, d_head, block_size, n_blocks, scale, dtype,
                             stream, key_new, value_new);
+}
+
+int pa_decode_shared_prefix(float* max_logits, float* exp_sums, float* tmp_out,
+                            int32_t partition_size, int32_t max_partitions,
+                            const void* key_new, const void* value_new, const void* q,
+                            void* k_pool, void* v_pool, const int32_t* block_table,
+                            int32_t max_blocks, const int32_t* context_lens, int32_t batch,
+                            int32_t n_kv_heads, int32_t gqa_group, int32_t d_head,
+                            int32_t block_size, int32_t n_blocks, int32_t prefix_len,
+                            float scale, int32_t dtype, void* stream) {
+  return decode_partitioned(max_logits, exp_sums, tmp_out, partition_size, max_partitions, q,
+                            k_pool, v_pool, block_table, max_blocks, context_lens, batch, 1,
+                            n_kv_heads, gqa_group, d_head, block_size, n_blocks, scale, dtype,
+                            stream, key_new, value_new, prefix_len);
 }
 
 int pa_decode_multi(float* max_logits, float* exp_sums, float* tmp_out, int32_t partition_size,

@@ -205,6 +205,10 @@ __global__ __launch_bounds__(kAttnThreads, PA_MFMA_MIN_BLOCKS) void attention_mf
   __shared__ float s_m[NW][16];
   __shared__ float s_l[NW][16];
   __shared__ int s_bad[NW];
+  // Shared-prefix launches: bit b set if sequence b's context length is
+  // invalid (negative or longer than its table); its columns of a shared
+  // item are written as NaN.
+  __shared__ uint32_t s_inval[kPlanBatch / 32];
   // Partitioned plan: exclusive prefix of the full partitions per sequence
   // (and the total), then the sequences in the order their final partitions
   // are dealt.  While it is built, the rings hold each sequence's sort key
@@ -236,29 +240,65 @@ __global__ __launch_bounds__(kAttnThreads, PA_MFMA_MIN_BLOCKS) void attention_mf
                 "the plan gives each thread 4 sequences and reads keys 16 at a time");
   // ---- item list
   int n_items, n_full = 0;
+  // Shared-prefix items: partitions p < npp of every sequence, prefix_seqs
+  // sequences (a group) per item; they come first in the plan, p-major, so
+  // the work groups of a column read the same prefix tiles at the same time.
+  int npp = 0, n_pre = 0, n_groups = 0;
   if (plan) {
     // Thread t owns sequences 4t..4t+3.  full(b) = partitions before b's
-    // last one, tail(b) = 1 if b has any; the exclusive prefix sum of
-    // full(b), and the rank of b's final partition among all final
-    // partitions by decreasing length (ties by sequence).
+    // last one (and past the shared prefix), tail(b) = 1 if b has any; the
+    // exclusive prefix sum of full(b), and the rank of b's final partition
+    // among all final partitions by decreasing length (ties by sequence).
     const int B = a.batch;
-    int fl[4], tl[4], key[4], fs = 0, ts = 0;
+    int fl[4], tl[4], key[4], cs[4], fs = 0, ts = 0;
     static_assert((int64_t)((1 << 20) - 1) * kPlanMaxBatch + kPlanMaxBatch < INT32_MAX, "plan keys fit 31 bits");
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       const int b = threadIdx.x * 4 + j;
-      int np = 0, c = 0;
+      cs[j] = b < B ? a.context_lens[b] : 0;
+    }
+    if (a.prefix_parts > 0) {
+      if (threadIdx.x < kPlanBatch / 32) s_inval[threadIdx.x] = 0u;
+      // Only partitions before every valid sequence's final one are shared
+      // items, so each sequence's final partition (the one holding the new
+      // token) stays its own item and no shared item needs a mask.
+      int cmin = INT32_MAX;
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        if (cs[j] >= 1 && (int64_t)cs[j] <= max_ctx) cmin = min(cmin, cs[j]);
+#pragma unroll
+      for (int d = 1; d < kWave; d <<= 1) cmin = min(cmin, shfl_xor_i(cmin, d));
+      if (lane == 0) s_bad[wave] = cmin;
+      __syncthreads();
+#pragma unroll
+      for (int w = 0; w < NW; ++w) cmin = min(cmin, s_bad[w]);
+      // uniform: keep the item decode below scalar
+      npp = __builtin_amdgcn_readfirstlane(
+          cmin == INT32_MAX ? 0 : min(min(a.prefix_parts, a.max_partitions), (cmin - 1) / P));
+      n_groups = (B + a.prefix_seqs - 1) / a.prefix_seqs;
+      n_pre = npp * n_groups;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int b = threadIdx.x * 4 + j;
+        if (b < B && (cs[j] < 0 || (int64_t)cs[j] > max_ctx))
+          atomicOr(&s_inval[b >> 5], 1u << (b & 31));
+      }
+    }
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int b = threadIdx.x * 4 + j;
+      int np = 0;
+      const int c = cs[j];
       if (b < B) {
-        c = a.context_lens[b];
         // more than max_partitions is an error reported by pa_reduce; the
         // cap keeps the item count in range
         np = c > 0 ? (int)min(((int64_t)c + P - 1) / P, (int64_t)a.max_partitions + 1) : 0;
       }
-      fl[j] = np > 0 ? np - 1 : 0;
-      tl[j] = np > 0 ? 1 : 0;
+      fl[j] = np > npp ? np - 1 - npp : 0;
+      tl[j] = np > npp ? 1 : 0;
       // final-partition length (capped at 2^20 - 1), ties broken by sequence:
       // distinct keys, larger first; no final partition or padding: below all
-      const int64_t len = np > 0 ? min((int64_t)c - (int64_t)(np - 1) * P, (int64_t)(1 << 20) - 1) : -1;
+      const int64_t len = np > npp ? min((int64_t)c - (int64_t)(np - 1) * P, (int64_t)(1 << 20) - 1) : -1;
       key[j] = len >= 0 ? (int)(len * kPlanMaxBatch + (kPlanMaxBatch - 1 - b)) : -1 - (b >= B);
       s_key[b] = key[j];
       s_rank[b] = 0;
@@ -311,7 +351,7 @@ __global__ __launch_bounds__(kAttnThreads, PA_MFMA_MIN_BLOCKS) void attention_mf
     if (threadIdx.x == 0) s_plan[B] = ftot;
     __syncthreads();
     n_full = ftot;
-    n_items = ftot + ttot;  // per column
+    n_items = n_pre + ftot + ttot;  // per column
   } else if (parts) {
     n_items = K * a.batch * a.max_partitions;
   } else {
@@ -345,14 +385,21 @@ __global__ __launch_bounds__(kAttnThreads, PA_MFMA_MIN_BLOCKS) void attention_mf
     }
     const int kvh = kh / a.n_hchunks;
     const int hc = kh - kvh * a.n_hchunks;
+    // pre: a shared-prefix item; b is then the group of sequences
+    // b * prefix_seqs .. + prefix_seqs - 1 (columns (sequence, head) pairs)
     int b, p = 0;
-    if (plan) {
-      if (rr < n_full) {
-        b = plan_search(s_plan, a.batch, rr);
-        p = rr - s_plan[b];
+    const bool pre = rr < n_pre;
+    if (pre) {
+      p = rr / n_groups;
+      b = rr - p * n_groups;
+    } else if (plan) {
+      const int r2 = rr - n_pre;
+      if (r2 < n_full) {
+        b = plan_search(s_plan, a.batch, r2);
+        p = r2 - s_plan[b] + npp;
       } else {
-        b = s_plan[kPlanMaxBatch + 1 + rr - n_full];
-        p = s_plan[b + 1] - s_plan[b];  // b's full partitions, then its tail
+        b = s_plan[kPlanMaxBatch + 1 + r2 - n_full];
+        p = s_plan[b + 1] - s_plan[b] + npp;  // b's full partitions, then its tail
       }
     } else if (parts) {
       const int j = rr / a.batch;
@@ -362,18 +409,28 @@ __global__ __launch_bounds__(kAttnThreads, PA_MFMA_MIN_BLOCKS) void attention_mf
     }
     b = __builtin_amdgcn_readfirstlane(b);
     p = __builtin_amdgcn_readfirstlane(p);
-    // a scalar read (the table and lengths are not written by this kernel)
-    const int ctx = ((const __attribute__((address_space(4))) int32_t*)a.context_lens)[b];
+    // first sequence of the item (its table row is the one read)
+    const int bseq = pre ? b * a.prefix_seqs : b;
+    // a scalar read (the table and lengths are not written by this kernel);
+    // a shared-prefix item's partition lies before every sequence's end
+    const int ctx = pre ? (p + 1) * P
+                        : ((const __attribute__((address_space(4))) int32_t*)a.context_lens)[b];
     const bool bad_ctx = ctx < 0 || (int64_t)ctx > max_ctx;
-    const int c0 = hc * 16;                // first column of the chunk
-    const int gv = min(16, G * NQ - c0);   // columns in the chunk
-    // row of column c0 + g (see above)
+    // columns per head of the group: query tokens, or a prefix item's sequences
+    const int nq = pre ? a.prefix_seqs : NQ;
+    const int nq_valid = pre ? min(nq, a.batch - bseq) : NQ;
+    const int c0 = hc * 16;                      // first column of the chunk
+    const int gv = min(16, G * nq_valid - c0);   // columns in the chunk
+    // row of column c0 + g (see above; a prefix item's column c is head
+    // c % G of sequence bseq + c / G)
     auto row_of = [&](int g) -> int64_t {
       const int c = c0 + g;
-      return (int64_t)(b * NQ + c / G) * Hq + kvh * G + c % G;
+      return (int64_t)(b * nq + c / G) * Hq + kvh * G + c % G;
     };
     int t0 = 0, t1 = ctx;
-    if (parts) {
+    if (pre) {
+      t0 = p * P;
+    } else if (parts) {
       const int64_t np = ctx > 0 ? ((int64_t)ctx + P - 1) / P : 0;
       if (!plan) {
         // one work group per (row, sequence): row j holds partition
@@ -424,7 +481,7 @@ __global__ __launch_bounds__(kAttnThreads, PA_MFMA_MIN_BLOCKS) void attention_mf
     // KV head in the pool, and the wave that owns that position's tile
     // patches it into the tile in LDS after the tile's copy lands (the copy
     // may predate the store), so the attention reads the new row either way.
-    const bool append = a.key_new != nullptr && t1 == ctx && ctx > 0;
+    const bool append = a.key_new != nullptr && t1 == ctx && ctx > 0 && !pre;
     const int tn = ctx - 1;
     const int ti_new = (tn - t0) >> 4;                     // its tile in the item
     const int wave_new = ti_new % NW, i_new = ti_new / NW, r_new = (tn - t0) & 15;
@@ -443,7 +500,7 @@ __global__ __launch_bounds__(kAttnThreads, PA_MFMA_MIN_BLOCKS) void attention_mf
     const char* vbase = (const char*)a.v_pool + kvh * head_bytes;
     const __attribute__((address_space(4))) int32_t* trow =
         (const __attribute__((address_space(4))) int32_t*)(a.block_table +
-                                                           (int64_t)b * a.max_blocks);
+                                                           (int64_t)bseq * a.max_blocks);
     char* my_ring = s_ring + wave * 4 * TILE;  // slot x: K at 2x*TILE, V at (2x+1)*TILE
     bool bad = false;
 
@@ -654,11 +711,17 @@ __global__ __launch_bounds__(kAttnThreads, PA_MFMA_MIN_BLOCKS) void attention_mf
     constexpr int NP = (16 * D4 + kAttnThreads - 1) / kAttnThreads;
     float mw[NP][NW], lw[NP][NW];
     f32x4_t ow[NP][NW];
+    bool colbad[NP];
 #pragma unroll
     for (int j = 0; j < NP; ++j) {
       const int idx = threadIdx.x + j * kAttnThreads;
+      colbad[j] = anybad;
       if (idx < gv * D4) {
         const int g = idx / D4, d = (idx - g * D4) * 4;
+        if (pre) {
+          const int sb = bseq + (c0 + g) / G;
+          colbad[j] |= ((s_inval[sb >> 5] >> (sb & 31)) & 1u) != 0u;
+        }
 #pragma unroll
         for (int w = 0; w < NW; ++w) {
           mw[j][w] = s_m[w][g];
@@ -687,13 +750,13 @@ __global__ __launch_bounds__(kAttnThreads, PA_MFMA_MIN_BLOCKS) void attention_mf
       // a column with no visible position in the partition: l = 0, o = 0
       f32x4_t r;
 #pragma unroll
-      for (int k = 0; k < 4; ++k) r[k] = anybad ? qnan : (L > 0.0f ? Ov[k] / L : 0.0f);
+      for (int k = 0; k < 4; ++k) r[k] = colbad[j] ? qnan : (L > 0.0f ? Ov[k] / L : 0.0f);
       if (parts) {
         const int64_t prow = row_of(g) * a.max_partitions + p;
         *reinterpret_cast<f32x4_t*>(&a.tmp_out[prow * D + d]) = r;
         if (d == 0) {
-          a.max_logits[prow] = anybad ? qnan : M * kLn2;
-          a.exp_sums[prow] = anybad ? qnan : L;
+          a.max_logits[prow] = colbad[j] ? qnan : M * kLn2;
+          a.exp_sums[prow] = colbad[j] ? qnan : L;
         }
       } else {
         const int64_t o = row_of(g) * D + d;

@@ -38,6 +38,12 @@ struct AttnArgs {
   int32_t max_partitions;
   int32_t persistent;  // partitioned launch sized to the GPU, items planned in-kernel
   int32_t n_queries;   // query tokens per sequence (the last n_queries positions)
+  // Shared prefix (persistent partitioned launches, n_queries == 1): the
+  // first prefix_parts partitions lie in blocks every table row shares, and
+  // one work item computes such a partition for prefix_seqs consecutive
+  // sequences at once (columns = (sequence, head) pairs).  0: off.
+  int32_t prefix_parts;
+  int32_t prefix_seqs;
   float scale_log2;    // scale * log2(e)
 };
 

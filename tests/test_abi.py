@@ -30,8 +30,8 @@ def declared_functions():
 def test_header_declares_the_entry_points():
     assert declared_functions() == sorted(
         ["pa_block_hashes", "pa_cache_write", "pa_copy_blocks", "pa_decode",
-         "pa_decode_multi", "pa_decode_partitioned", "pa_decode_step",
-         "pa_pool_alloc",
+         "pa_decode_multi", "pa_decode_partitioned",
+         "pa_decode_shared_prefix", "pa_decode_step", "pa_pool_alloc",
          "pa_pool_available", "pa_pool_create", "pa_pool_destroy",
          "pa_pool_fork", "pa_pool_map_prefix", "pa_pool_refcount",
          "pa_pool_release", "pa_reduce", "pa_strerror"])
@@ -200,6 +200,32 @@ def test_step_argument_checks(lib):
     assert _step(lib, kn=MIS) == PA_ERR_ALIGN
     assert _step(lib, psz=8) == PA_ERR_PARTITION
     assert _step(lib, d=32) == PA_ERR_UNSUPPORTED
+
+
+def _prefix(lib, **kw):
+    a = dict(ml=P, es=P, to=P, psz=512, pmax=4, kn=P, vn=P, q=P, k=P, v=P,
+             tbl=P, mb=64, ctx=P, B=4, hkv=2, G=4, d=128, bs=16, nb=32,
+             plen=512, scale=0.1, dt=2)
+    a.update(kw)
+    return lib.pa_decode_shared_prefix(
+        a["ml"], a["es"], a["to"], a["psz"], a["pmax"], a["kn"], a["vn"],
+        a["q"], a["k"], a["v"], a["tbl"], a["mb"], a["ctx"], a["B"], a["hkv"],
+        a["G"], a["d"], a["bs"], a["nb"], a["plen"], a["scale"], a["dt"],
+        None)
+
+
+def test_shared_prefix_argument_checks(lib):
+    assert _prefix(lib, B=0) == PA_OK
+    for k in ("ml", "es", "to", "q", "k", "v", "tbl", "ctx"):
+        assert _prefix(lib, **{k: None}) == PA_ERR_NULL, k
+    # the new rows are optional, but only as a pair
+    assert _prefix(lib, kn=None) == PA_ERR_NULL
+    assert _prefix(lib, vn=None) == PA_ERR_NULL
+    assert _prefix(lib, kn=MIS) == PA_ERR_ALIGN
+    assert _prefix(lib, plen=-1) == PA_ERR_SHAPE
+    assert _prefix(lib, psz=8) == PA_ERR_PARTITION
+    assert _prefix(lib, pmax=0) == PA_ERR_WORKSPACE
+    assert _prefix(lib, d=32) == PA_ERR_UNSUPPORTED
 
 
 def _red(lib, **kw):
