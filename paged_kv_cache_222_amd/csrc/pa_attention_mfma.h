@@ -33,7 +33,10 @@
 // persistent: every work group derives the same item list from the context
 // lengths (full partitions, then final partitions longest first) and takes
 // its items in a back-and-forth deal over the work groups of its column.
-// No work group is launched for an empty partition.
+// No work group is launched for an empty partition.  With a shared prefix
+// (blocks every table row shares) its partitions are items of their own,
+// each for up to 16 / G sequences -- columns (sequence, head) pairs -- so a
+// prefix tile is read once per such group rather than once per sequence.
 #pragma once
 
 #include <type_traits>
@@ -241,8 +244,9 @@ __global__ __launch_bounds__(kAttnThreads, PA_MFMA_MIN_BLOCKS) void attention_mf
   // ---- item list
   int n_items, n_full = 0;
   // Shared-prefix items: partitions p < npp of every sequence, prefix_seqs
-  // sequences (a group) per item; they come first in the plan, p-major, so
-  // the work groups of a column read the same prefix tiles at the same time.
+  // sequences (a group) per item, p-major, so the work groups of a column
+  // read the same prefix tiles at about the same time; in the plan they
+  // alternate with the full private partitions.
   int npp = 0, n_pre = 0, n_groups = 0;
   if (plan) {
     // Thread t owns sequences 4t..4t+3.  full(b) = partitions before b's
@@ -388,12 +392,30 @@ __global__ __launch_bounds__(kAttnThreads, PA_MFMA_MIN_BLOCKS) void attention_mf
     // pre: a shared-prefix item; b is then the group of sequences
     // b * prefix_seqs .. + prefix_seqs - 1 (columns (sequence, head) pairs)
     int b, p = 0;
-    const bool pre = rr < n_pre;
+    bool pre = false;
+    int rp = 0, r2 = rr;   // index among shared items / among the rest
+    if (n_pre > 0) {
+      // shared items alternate with full partitions, so the L2-bound shared
+      // reads overlap the HBM-bound private ones (all shared items first:
+      // 609 instead of 590 us on the shared-prefix batch, P 2048)
+      const int m2 = min(n_pre, n_full);
+      if (rr < 2 * m2) {
+        pre = (rr & 1) == 0;
+        rp = rr >> 1;
+        r2 = rr >> 1;
+      } else if (rr < n_pre + n_full) {
+        pre = n_pre > n_full;
+        rp = rr - m2;
+        r2 = rr - m2;
+      } else {
+        pre = false;
+        r2 = rr - n_pre;
+      }
+    }
     if (pre) {
-      p = rr / n_groups;
-      b = rr - p * n_groups;
+      p = rp / n_groups;
+      b = rp - p * n_groups;
     } else if (plan) {
-      const int r2 = rr - n_pre;
       if (r2 < n_full) {
         b = plan_search(s_plan, a.batch, r2);
         p = r2 - s_plan[b] + npp;
