@@ -58,6 +58,9 @@ def parse():
                          "step (the shared-prefix step for a batch with a "
                          "shared prefix); best: report the fastest form")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-read-ceiling", action="store_true",
+                    help="skip the read-ceiling calibration (pa_read_ceiling "
+                         "over a 4 GiB buffer) after the decode timing")
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
                     help="budget of the CPU oracle sample")
     ap.add_argument("--op", choices=["decode", "copy-blocks", "verify",
@@ -130,6 +133,38 @@ def measured_traffic(name, variant, P):
         return int(kv["traffic_bytes_per_launch"])
     except (KeyError, ValueError):
         return None
+
+
+def measure_read_ceiling(torch, pa, gib=4, reps=10):
+    """The device's achievable HBM read rate for the attention kernels'
+    access pattern: pa_read_ceiling over a ``gib`` GiB buffer, in address
+    order and as a gather of its 4 KiB tiles in a random order (median of
+    ``reps`` launches timed with HIP events on torch's current stream, the
+    stream the launches go to)."""
+    nbytes = gib << 30
+    buf = torch.zeros(nbytes // 4, dtype=torch.int32, device="cuda")
+    n_tiles = nbytes // 4096
+    gen = torch.Generator(device="cpu").manual_seed(0)
+    order = torch.randperm(n_tiles, generator=gen).to(torch.int32).cuda()
+    sink = torch.zeros(1, dtype=torch.int32, device="cuda")
+    res = {"buffer_bytes": nbytes, "tile_bytes": 4096}
+    for name, kw in (("stream", {}), ("tile_gather", {"tile_order": order})):
+        for _ in range(2):
+            pa.pa_read_ceiling(buf, sink, **kw)
+        torch.cuda.synchronize()
+        ts = []
+        for _ in range(reps):
+            e0, e1 = (torch.cuda.Event(enable_timing=True) for _ in range(2))
+            e0.record()
+            pa.pa_read_ceiling(buf, sink, **kw)
+            e1.record()
+            torch.cuda.synchronize()
+            ts.append(e0.elapsed_time(e1))
+        ms = float(np.median(ts))
+        res[f"{name}_GBs"] = round(nbytes / (ms * 1e-3) / 1e9, 1)
+    del buf, order
+    torch.cuda.empty_cache()
+    return res
 
 
 def copy_calibration(mib):
@@ -653,6 +688,13 @@ def main():
                      "algorithmic_bytes_per_launch": alg,
                      "avg_launch_us": round(attn_us, 3)},
     }
+    if not args.no_read_ceiling:
+        log("measuring the read ceiling (4 GiB, stream and 4 KiB-tile gather)")
+        del copies
+        rc = measure_read_ceiling(torch, pa)
+        rc["attention_frac_of_tile_gather"] = round(
+            achieved / rc["tile_gather_GBs"], 4)
+        rec["read_ceiling"] = rc
     if not args.no_cpu_baseline:
         log("timing the fp64 CPU oracle on a sample")
         rec["cpu_baseline"] = cpu_baseline(w, args.cpu_seconds)

@@ -116,6 +116,28 @@ int pa_copy_blocks(void* k_pool, void* v_pool, const int32_t* block_pairs,
                    void* stream);
 
 /*
+ * pa_read_ceiling -- a measurement aid, not part of the decode path: reads
+ * n_tiles tiles of tile_bytes bytes from buf (tile ids tile_order[i], or
+ * 0 .. n_tiles - 1 in address order when tile_order is NULL) with the
+ * non-temporal 16-byte loads the attention kernels use, and nothing else.
+ * Timed on its own it gives the device's achievable HBM read rate for that
+ * access pattern -- sequential, or a gather of 4 KiB tiles scattered like
+ * the cache's (block, KV head) tiles -- the ceiling the attention kernels'
+ * rates are compared with (the decode path itself is bound by HBM reads:
+ * "Serving" section 23.2).  Tile ids outside the buffer are skipped.  sink
+ * is written only in the (practically impossible) case that the folded
+ * bytes equal a fixed constant; it keeps the loads from being removed.
+ *
+ *   buf         [buf_bytes] bytes, 16-byte aligned, read
+ *   tile_order  [n_tiles] int32, or NULL (then n_tiles <= buf_bytes / tile_bytes)
+ *   tile_bytes  a positive multiple of 16 (PA_ERR_SHAPE otherwise)
+ *   sink        one uint32
+ */
+int pa_read_ceiling(const void* buf, int64_t buf_bytes, const int32_t* tile_order,
+                    int64_t n_tiles, int32_t tile_bytes, uint32_t* sink,
+                    void* stream);
+
+/*
  * pa_decode -- one query token per sequence attends over all its cached
  * positions, in one pass per (sequence, KV head).
  *

@@ -72,6 +72,8 @@ def load() -> ctypes.CDLL:
                                                 vp, vp, vp, vp, i32, vp, i32,
                                                 i32, i32, i32, i32, i32, i32,
                                                 f32, i32, vp]
+        lib.pa_read_ceiling.argtypes = [vp, ctypes.c_int64, vp, ctypes.c_int64,
+                                        i32, vp, vp]
         lib.pa_decode.argtypes = [vp, vp, vp, vp, vp, i32, vp, i32, i32, i32,
                                   i32, i32, i32, f32, i32, vp]
         lib.pa_decode_partitioned.argtypes = [vp, vp, vp, i32, i32, vp, vp, vp,
@@ -81,7 +83,7 @@ def load() -> ctypes.CDLL:
                                   i32, vp]
         for fn in ("pa_cache_write", "pa_copy_blocks", "pa_decode",
                    "pa_decode_partitioned", "pa_decode_multi", "pa_decode_step",
-                   "pa_decode_shared_prefix", "pa_reduce"):
+                   "pa_decode_shared_prefix", "pa_reduce", "pa_read_ceiling"):
             getattr(lib, fn).restype = ctypes.c_int
         u64p = ctypes.POINTER(ctypes.c_uint64)
         i32p = ctypes.POINTER(ctypes.c_int32)
@@ -339,6 +341,33 @@ def pa_decode_shared_prefix(max_logits, exp_sums, tmp_out, q, k_pool, v_pool,
         block_table.data_ptr(), mb, context_lens.data_ptr(), B, n_kv, G, d, bs,
         n_blocks, int(prefix_len), float(scale), _dtype_code(q),
         _stream(stream)))
+
+
+def pa_read_ceiling(buf, sink, *, tile_order=None, n_tiles=None,
+                    tile_bytes=4096, stream=None):
+    """Read tiles of ``buf`` (a contiguous device tensor) in ``tile_order``
+    (int32 device tensor) or in address order, loads only: the calibration
+    of the device's achievable HBM read rate.  ``sink`` is a one-element
+    int32 device tensor."""
+    torch = _torch()
+    lib = load()
+    if not (buf.is_cuda and buf.is_contiguous()):
+        raise ValueError("buf must be a contiguous device tensor")
+    _dev("sink", sink, torch.int32, 1)
+    nbytes = buf.numel() * buf.element_size()
+    order = None
+    if tile_order is not None:
+        _dev("tile_order", tile_order, torch.int32, 1)
+        order = tile_order.data_ptr()
+        if n_tiles is None:
+            n_tiles = tile_order.numel()
+        elif n_tiles > tile_order.numel():
+            raise ValueError("n_tiles exceeds tile_order")
+    elif n_tiles is None:
+        n_tiles = nbytes // int(tile_bytes)
+    _check("pa_read_ceiling", lib.pa_read_ceiling(
+        buf.data_ptr(), nbytes, order, int(n_tiles), int(tile_bytes),
+        sink.data_ptr(), _stream(stream)))
 
 
 def pa_decode_multi(max_logits, exp_sums, tmp_out, q, k_pool, v_pool,

@@ -287,6 +287,34 @@ int pa_copy_blocks(void* k_pool, void* v_pool, const int32_t* block_pairs, int32
   return launch_status(pa::launch_copy_blocks(a, (hipStream_t)stream));
 }
 
+int pa_read_ceiling(const void* buf, int64_t buf_bytes, const int32_t* tile_order,
+                    int64_t n_tiles, int32_t tile_bytes, uint32_t* sink, void* stream) {
+  if (n_tiles < 0 || buf_bytes < 0) return PA_ERR_SHAPE;
+  if (n_tiles == 0) return PA_OK;
+  if (!buf || !sink) return PA_ERR_NULL;
+  if (tile_bytes <= 0 || tile_bytes % 16 != 0) return PA_ERR_SHAPE;
+  const int64_t buf_tiles = buf_bytes / tile_bytes;
+  if (n_tiles > INT_MAX || buf_tiles > INT_MAX) return PA_ERR_SHAPE;
+  if (!tile_order && n_tiles > buf_tiles) return PA_ERR_SHAPE;
+  if (!aligned16(buf) || !aligned4(sink) || (tile_order && !aligned4(tile_order)))
+    return PA_ERR_ALIGN;
+  int cus = 0, dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess ||
+      hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+      cus < 1)
+    cus = 256;
+  pa::ReadCeilingArgs a{};
+  a.buf = buf;
+  a.tile_order = tile_order;
+  a.sink = sink;
+  a.n_tiles = n_tiles;
+  a.buf_tiles = buf_tiles;
+  a.tile_bytes = tile_bytes;
+  const int64_t grid = std::min<int64_t>((int64_t)cus * 8, n_tiles);
+  (void)hipGetLastError();
+  return launch_status(pa::launch_read_ceiling(a, (unsigned)grid, (hipStream_t)stream));
+}
+
 int pa_decode(void* out, const void* q, const void* k_pool, const void* v_pool,
               const int32_t* block_table, int32_t max_blocks, const int32_t* context_lens,
               int32_t batch, int32_t n_kv_heads, int32_t gqa_group, int32_t d_head,

@@ -103,6 +103,18 @@ struct CopyBlocksArgs {
   int64_t block_bytes;         // n_kv_heads * block_size * d_head * element size
 };
 
+constexpr int kReadThreads = 256;
+constexpr int kReadUnroll = 8;   // tiles whose loads are in flight together
+
+struct ReadCeilingArgs {
+  const void* buf;
+  const int32_t* tile_order;  // null: tiles in address order
+  uint32_t* sink;
+  int64_t n_tiles;            // tiles to read
+  int64_t buf_tiles;          // tiles in the buffer (ids outside are skipped)
+  int64_t tile_bytes;         // a multiple of 16
+};
+
 // Each returns a hipError_t from the launch.
 hipError_t launch_attention_f32(const AttnArgs& a, int d_head, int heads_per_chunk,
                                 unsigned grid, hipStream_t s);
@@ -116,6 +128,7 @@ hipError_t launch_reduce(const ReduceArgs& a, int dtype, int d_head, hipStream_t
 hipError_t launch_cache_write(const CacheWriteArgs& a, hipStream_t s);
 hipError_t launch_append(const AppendArgs& a, hipStream_t s);
 hipError_t launch_copy_blocks(const CopyBlocksArgs& a, hipStream_t s);
+hipError_t launch_read_ceiling(const ReadCeilingArgs& a, unsigned grid, hipStream_t s);
 
 constexpr int kAttnThreads = 256;  // four waves per work item
 constexpr int kMfmaHeads = 16;     // columns (query token, head pairs) per matrix-core work item

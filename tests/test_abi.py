@@ -34,7 +34,7 @@ def test_header_declares_the_entry_points():
          "pa_decode_shared_prefix", "pa_decode_step", "pa_pool_alloc",
          "pa_pool_available", "pa_pool_create", "pa_pool_destroy",
          "pa_pool_fork", "pa_pool_map_prefix", "pa_pool_refcount",
-         "pa_pool_release", "pa_reduce", "pa_strerror"])
+         "pa_pool_release", "pa_read_ceiling", "pa_reduce", "pa_strerror"])
 
 
 def test_library_exports_every_declared_symbol(lib):
@@ -226,6 +226,25 @@ def test_shared_prefix_argument_checks(lib):
     assert _prefix(lib, psz=8) == PA_ERR_PARTITION
     assert _prefix(lib, pmax=0) == PA_ERR_WORKSPACE
     assert _prefix(lib, d=32) == PA_ERR_UNSUPPORTED
+
+
+def _ceil(lib, **kw):
+    a = dict(buf=P, nb=1 << 20, order=None, n=256, tb=4096, sink=P)
+    a.update(kw)
+    return lib.pa_read_ceiling(a["buf"], a["nb"], a["order"], a["n"], a["tb"],
+                               a["sink"], None)
+
+
+def test_read_ceiling_argument_checks(lib):
+    assert _ceil(lib, n=0) == PA_OK
+    assert _ceil(lib, n=-1) == PA_ERR_SHAPE
+    assert _ceil(lib, buf=None) == PA_ERR_NULL
+    assert _ceil(lib, sink=None) == PA_ERR_NULL
+    assert _ceil(lib, tb=24) == PA_ERR_SHAPE
+    assert _ceil(lib, tb=0) == PA_ERR_SHAPE
+    assert _ceil(lib, n=257) == PA_ERR_SHAPE        # past the buffer, no order
+    assert _ceil(lib, buf=MIS) == PA_ERR_ALIGN
+    assert _ceil(lib, order=P + 2, n=300) == PA_ERR_ALIGN
 
 
 def _red(lib, **kw):
