@@ -205,3 +205,56 @@ def test_full_shared_prefix_batch(pa, bs):
     print(f"shared-prefix bs{bs}: max err {err:.3g} on {len(rows)} rows")
     assert err <= TOL["bf16"]
     assert np.isfinite(got).all()
+
+
+def _step_reference(pa, w, P):
+    """pa_decode_step + pa_reduce on a fresh upload of w."""
+    d = DeviceBatch(w)
+    B, Hq, D = d.q.shape
+    ws = pa.partition_workspace(B, Hq, D, -(-int(w.context_lens.max()) // P))
+    note(f"pa_decode_step reference P={P}")
+    pa.pa_decode_step(*ws, d.key_new, d.value_new, d.q, d.k_pool, d.v_pool,
+                      d.block_table, d.context_lens, partition_size=P,
+                      scale=d.scale)
+    out = d.empty_out()
+    pa.pa_reduce(out, *ws, d.context_lens, partition_size=P)
+    torch.cuda.synchronize()
+    return d, out
+
+
+def test_zero_prefix_is_decode_step_bit_for_bit(pa):
+    ctx = [300 + 37 * i for i in range(11)]
+    w = wl.make_custom(ctx, n_q_heads=32, n_kv_heads=8, d_head=128,
+                       block_size=16, dtype="bf16", seed=21, prefix_len=256)
+    d1 = DeviceBatch(w)
+    out1, _ = _run(pa, d1, 128, 0, write=True, name="prefix_len 0")
+    d2, out2 = _step_reference(pa, w, 128)
+    assert from_dev(out1).tobytes() == from_dev(out2).tobytes()
+    assert from_dev(d1.k_pool).tobytes() == from_dev(d2.k_pool).tobytes()
+
+
+@pytest.mark.parametrize("case", ["f32", "batch over 1024"])
+def test_paths_without_shared_items(pa, case):
+    """fp32 (vector-ALU kernel) and batches beyond the in-kernel plan run
+    every row through its own table: the result of pa_decode_step, bit for
+    bit, and within the tolerance of the oracle."""
+    if case == "f32":
+        ctx = [70, 90, 65, 130, 81]
+        w = wl.make_custom(ctx, n_q_heads=4, n_kv_heads=2, d_head=64,
+                           block_size=16, dtype="f32", seed=22, prefix_len=64)
+        P = 32
+    else:
+        rng = np.random.default_rng(23)
+        ctx = [64 + int(s) for s in rng.integers(1, 40, size=1030)]
+        w = wl.make_custom(ctx, n_q_heads=4, n_kv_heads=1, d_head=64,
+                           block_size=16, dtype="f16", seed=23, prefix_len=64)
+        P = 32
+    d1 = DeviceBatch(w)
+    out1, _ = _run(pa, d1, P, 64, write=True, name=case)
+    _, out2 = _step_reference(pa, w, P)
+    assert from_dev(out1).tobytes() == from_dev(out2).tobytes()
+    k_ref, v_ref = oracle_pools_after_write(w)
+    assert from_dev(d1.k_pool).tobytes() == k_ref.tobytes()
+    ref = oracle_out(w, k_ref, v_ref)
+    err = np.abs(as_f64(out1) - ref)
+    assert (err <= TOL[w.cfg.dtype] + rounding_bound(ref, w.cfg.dtype)).all()
