@@ -4,7 +4,8 @@
 // and o_p the normalised partial output.  Then l_p exp(m_p) is that
 // partition's softmax denominator, and attention over the whole context is
 // the mean of the o_p weighted by w_p = l_p exp(m_p - M), M = max_p m_p.
-// One wave per (sequence, query head); lanes own d_head/64 output elements.
+// One wave per (sequence, query head), four per work group; lanes own
+// d_head/64 output elements.
 #include "pa_device.h"
 #include "pa_launch.h"
 
@@ -15,12 +16,20 @@ namespace pa {
 // once, then the partitions past the sequence's end are masked, so the row
 // costs one memory round trip instead of three.
 constexpr int kFewParts = 8;
+// (sequence, query head) rows per work group, one wave each: fewer, larger
+// work groups are dispatched faster than one 64-thread group per row.
+#ifndef PA_REDUCE_ROWS
+#define PA_REDUCE_ROWS 4
+#endif
+constexpr int kRedRows = PA_REDUCE_ROWS;
 
 template <Dt DT, int D>
-__global__ __launch_bounds__(kWave) void reduce_few_kernel(ReduceArgs a) {
+__global__ __launch_bounds__(kWave * kRedRows) void reduce_few_kernel(ReduceArgs a) {
   constexpr int DPL = D / kWave;
-  const int lane = threadIdx.x;
-  const int bh = blockIdx.x;
+  const int lane = threadIdx.x & (kWave - 1);
+  const int64_t bh64 = (int64_t)blockIdx.x * kRedRows + threadIdx.x / kWave;
+  if (bh64 >= (int64_t)a.batch * a.n_q_heads) return;
+  const int bh = (int)bh64;
   const int b = bh / a.n_q_heads;
   const int PM = a.max_partitions;  // <= kFewParts
   const float* ml = a.max_logits + (int64_t)bh * PM;
@@ -71,10 +80,12 @@ __global__ __launch_bounds__(kWave) void reduce_few_kernel(ReduceArgs a) {
 }
 
 template <Dt DT, int D>
-__global__ __launch_bounds__(kWave) void reduce_kernel(ReduceArgs a) {
+__global__ __launch_bounds__(kWave * kRedRows) void reduce_kernel(ReduceArgs a) {
   constexpr int DPL = D / kWave;  // output elements per lane
-  const int lane = threadIdx.x;
-  const int bh = blockIdx.x;  // b * n_q_heads + h
+  const int lane = threadIdx.x & (kWave - 1);
+  const int64_t bh64 = (int64_t)blockIdx.x * kRedRows + threadIdx.x / kWave;
+  if (bh64 >= (int64_t)a.batch * a.n_q_heads) return;
+  const int bh = (int)bh64;  // b * n_q_heads + h
   const int b = bh / a.n_q_heads;
   const int ctx = a.context_lens[b];
   const int P = a.partition_size;
@@ -140,18 +151,18 @@ __global__ __launch_bounds__(kWave) void reduce_kernel(ReduceArgs a) {
 
 template <Dt DT>
 static hipError_t launch_reduce_dt(const ReduceArgs& a, int d_head, hipStream_t s) {
-  const unsigned grid = (unsigned)(a.batch * a.n_q_heads);
+  const unsigned grid = (unsigned)(((int64_t)a.batch * a.n_q_heads + kRedRows - 1) / kRedRows);
   const bool few = a.max_partitions <= kFewParts;
   if (d_head == 64) {
     if (few)
-      hipLaunchKernelGGL((reduce_few_kernel<DT, 64>), dim3(grid), dim3(kWave), 0, s, a);
+      hipLaunchKernelGGL((reduce_few_kernel<DT, 64>), dim3(grid), dim3(kWave * kRedRows), 0, s, a);
     else
-      hipLaunchKernelGGL((reduce_kernel<DT, 64>), dim3(grid), dim3(kWave), 0, s, a);
+      hipLaunchKernelGGL((reduce_kernel<DT, 64>), dim3(grid), dim3(kWave * kRedRows), 0, s, a);
   } else if (d_head == 128) {
     if (few)
-      hipLaunchKernelGGL((reduce_few_kernel<DT, 128>), dim3(grid), dim3(kWave), 0, s, a);
+      hipLaunchKernelGGL((reduce_few_kernel<DT, 128>), dim3(grid), dim3(kWave * kRedRows), 0, s, a);
     else
-      hipLaunchKernelGGL((reduce_kernel<DT, 128>), dim3(grid), dim3(kWave), 0, s, a);
+      hipLaunchKernelGGL((reduce_kernel<DT, 128>), dim3(grid), dim3(kWave * kRedRows), 0, s, a);
   } else {
     return hipErrorInvalidValue;
   }
