@@ -110,13 +110,16 @@ def kernel_source_hash():
     return h.hexdigest()[:16]
 
 
-def measured_traffic(name, variant, P):
+def measured_traffic(name, variant, P, block_size):
     """HBM bytes per attention launch from the counter summary stored under
     profiles/ (FETCH_SIZE + WRITE_SIZE, each scaled by the copy-kernel
     factor), or None when there is none for this workload or the kernel
     sources changed since it was taken."""
     path = os.path.join(ROOT, "profiles",
-                        f"attention_mfma_{name}_hbm_counters.txt")
+                        f"attention_mfma_{name}_P{P}_hbm_counters.txt")
+    if not os.path.exists(path):
+        path = os.path.join(ROOT, "profiles",
+                            f"attention_mfma_{name}_hbm_counters.txt")
     if not os.path.exists(path):
         return None
     kv = {}
@@ -127,7 +130,8 @@ def measured_traffic(name, variant, P):
                 kv[k.strip()] = v.strip()
     if (kv.get("source_sha256_16") != kernel_source_hash()
             or kv.get("variant") != variant
-            or kv.get("partition_size") != str(P)):
+            or kv.get("partition_size") != str(P)
+            or kv.get("block_size", "16") != str(block_size)):
         return None
     try:
         return int(kv["traffic_bytes_per_launch"])
@@ -684,7 +688,7 @@ def main():
         "roofline": {"kernel": kernel, "bound": "hbm",
                      "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
-                     "traffic": measured_traffic(c.name, best, P),
+                     "traffic": measured_traffic(c.name, best, P, c.block_size),
                      "algorithmic_bytes_per_launch": alg,
                      "avg_launch_us": round(attn_us, 3)},
     }
