@@ -240,7 +240,7 @@ __global__ __launch_bounds__(kAttnThreads, PA_MFMA_MIN_BLOCKS) void attention_mf
   const int64_t max_ctx = (int64_t)a.max_blocks << a.block_shift;
 
   static_assert(kPlanMaxBatch == 4 * kAttnThreads && kPlanMaxBatch % 16 == 0,
-                "the plan gives each thread 4 sequences and reads keys 16 at a time");
+                "the plan gives each thread 4 sequences");
   // ---- item list
   int n_items, n_full = 0;
   // Shared-prefix items: partitions p < npp of every sequence, prefix_seqs
@@ -323,22 +323,31 @@ __global__ __launch_bounds__(kAttnThreads, PA_MFMA_MIN_BLOCKS) void attention_mf
       ftot += fw;
       ttot += tw;
     }
-    // rank(b) = number of keys above b's; the B x B comparisons are split
-    // into (sequence, 16 keys) units over all threads and summed in LDS
-    // (integer sums: the result does not depend on the order).
+    // rank(b) = number of keys above b's.  A group of tps consecutive
+    // threads (one thread per sequence from B = 256 on, up to 16 for small
+    // batches) counts for one sequence, each thread over every tps-th block
+    // of 4 keys, and the group sums its counts with lane exchanges; the
+    // threads of a wave read at most tps different key addresses at once
+    // (LDS broadcast).  Integer counts: the result does not depend on the
+    // order.  (Splitting the comparisons into (sequence, 16 keys) units
+    // summed with LDS atomics took ~9 us at B = 256: the atomics of one
+    // sequence serialise.)
     {
-      const int ng = (B + 15) >> 4;
       const int4* keys4 = reinterpret_cast<const int4*>(s_key);
-      for (int u = threadIdx.x; u < B * ng; u += kAttnThreads) {
-        const int b = u / ng, g = u - (u / ng) * ng;
+      const int nk4 = (B + 3) >> 2;   // keys past B are padding, below all
+      const int tps = B >= 256 ? 1 : B >= 128 ? 2 : B >= 64 ? 4 : B >= 32 ? 8 : 16;
+      const int part = threadIdx.x & (tps - 1);
+      for (int b = threadIdx.x / tps; b < B; b += kAttnThreads / tps) {
         const int kb = s_key[b];
         int cnt = 0;
-#pragma unroll
-        for (int v = 0; v < 4; ++v) {
-          const int4 k4 = keys4[g * 4 + v];
+#pragma unroll 4
+        for (int g = part; g < nk4; g += tps) {
+          const int4 k4 = keys4[g];
           cnt += (k4.x > kb) + (k4.y > kb) + (k4.z > kb) + (k4.w > kb);
         }
-        atomicAdd(&s_rank[b], cnt);
+        // the group's lanes are all in this iteration (same b)
+        for (int d = 1; d < tps; d <<= 1) cnt += shfl_xor_i(cnt, d);
+        if (part == 0) s_rank[b] = cnt;
       }
     }
     __syncthreads();
