@@ -324,30 +324,46 @@ __global__ __launch_bounds__(kAttnThreads, PA_MFMA_MIN_BLOCKS) void attention_mf
       ttot += tw;
     }
     // rank(b) = number of keys above b's.  A group of tps consecutive
-    // threads (one thread per sequence from B = 256 on, up to 16 for small
-    // batches) counts for one sequence, each thread over every tps-th block
-    // of 4 keys, and the group sums its counts with lane exchanges; the
-    // threads of a wave read at most tps different key addresses at once
-    // (LDS broadcast).  Integer counts: the result does not depend on the
-    // order.  (Splitting the comparisons into (sequence, 16 keys) units
-    // summed with LDS atomics took ~9 us at B = 256: the atomics of one
-    // sequence serialise.)
+    // threads counts for 4 consecutive sequences (their keys in registers),
+    // each thread over every tps-th block of 4 keys, so each key read serves
+    // 16 comparisons; the group sums its counts with lane exchanges.  tps =
+    // 1024 / B (B rounded up to a power of two, at least 16) gives one pass
+    // over all sequences.  The threads of a wave read at most tps key
+    // addresses at once (LDS broadcast).  Integer counts: the result does
+    // not depend on the order.  (Summing (sequence, 16 keys) units with LDS
+    // atomics took ~9 us at B = 256; one thread per sequence, ~3.8 us.)
     {
       const int4* keys4 = reinterpret_cast<const int4*>(s_key);
       const int nk4 = (B + 3) >> 2;   // keys past B are padding, below all
-      const int tps = B >= 256 ? 1 : B >= 128 ? 2 : B >= 64 ? 4 : B >= 32 ? 8 : 16;
+      int bp = 16;
+      while (bp < B) bp <<= 1;
+      const int tps = min(kWave, kPlanMaxBatch / bp);
       const int part = threadIdx.x & (tps - 1);
-      for (int b = threadIdx.x / tps; b < B; b += kAttnThreads / tps) {
-        const int kb = s_key[b];
-        int cnt = 0;
+      for (int grp = threadIdx.x / tps; 4 * grp < B; grp += kAttnThreads / tps) {
+        const int4 kb = keys4[grp];
+        int c0 = 0, c1 = 0, c2 = 0, c3 = 0;
 #pragma unroll 4
         for (int g = part; g < nk4; g += tps) {
           const int4 k4 = keys4[g];
-          cnt += (k4.x > kb) + (k4.y > kb) + (k4.z > kb) + (k4.w > kb);
+          c0 += (k4.x > kb.x) + (k4.y > kb.x) + (k4.z > kb.x) + (k4.w > kb.x);
+          c1 += (k4.x > kb.y) + (k4.y > kb.y) + (k4.z > kb.y) + (k4.w > kb.y);
+          c2 += (k4.x > kb.z) + (k4.y > kb.z) + (k4.z > kb.z) + (k4.w > kb.z);
+          c3 += (k4.x > kb.w) + (k4.y > kb.w) + (k4.z > kb.w) + (k4.w > kb.w);
         }
-        // the group's lanes are all in this iteration (same b)
-        for (int d = 1; d < tps; d <<= 1) cnt += shfl_xor_i(cnt, d);
-        if (part == 0) s_rank[b] = cnt;
+        // the group's lanes are all in this iteration (same grp)
+        for (int d = 1; d < tps; d <<= 1) {
+          c0 += shfl_xor_i(c0, d);
+          c1 += shfl_xor_i(c1, d);
+          c2 += shfl_xor_i(c2, d);
+          c3 += shfl_xor_i(c3, d);
+        }
+        if (part == 0) {
+          const int b0 = 4 * grp;
+          s_rank[b0] = c0;   // b0 < B
+          if (b0 + 1 < B) s_rank[b0 + 1] = c1;
+          if (b0 + 2 < B) s_rank[b0 + 2] = c2;
+          if (b0 + 3 < B) s_rank[b0 + 3] = c3;
+        }
       }
     }
     __syncthreads();
