@@ -186,12 +186,12 @@ CONFIGS: Dict[str, Config] = {
         name="llama3-8b", batch=128, n_q_heads=32, n_kv_heads=8, d_head=128,
         block_size=16, dtype="bf16", max_context=8192,
         lengths=_lognormal(1024, 1.0, 16, 8192),
-        # not fixed by the workload: the fastest of 512/1024/2048/4096 on
-        # MI355X (attention 159.6/148.4/146.9/147.9 us per step)
-        partition_size=2048,
+        # not fixed by the workload: the fastest of 1536..4096 on MI355X
+        # (step 155.7/151.4/153.4/147.5/152.8 us at 1536/2048/2560/3072/4096)
+        partition_size=3072,
         description="GQA 32/8 heads, d128, bf16, B=128, ctx log-normal "
                     "(median 1024, sigma 1) clipped to [16, 8192], "
-                    "2048-token partitions"),
+                    "3072-token partitions"),
     "shared-prefix": Config(
         name="shared-prefix", batch=256, n_q_heads=32, n_kv_heads=8,
         d_head=128, block_size=16, dtype="bf16", max_context=2048 + 6144,

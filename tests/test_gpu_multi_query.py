@@ -75,7 +75,7 @@ def test_multi_query_small(pa, dtype, D, BS, Hkv, G, k, P):
 
 def test_multi_query_llama3_sampled_rows(pa):
     """The LLaMA-3-8B batch (B=128, 32/8 heads, d128, bf16, log-normal
-    lengths) with 4 query tokens at partition 2048: every token and head of
+    lengths) with 4 query tokens at its partition size: every token and head of
     8 sequences, the longest and the shortest among them."""
     w = wl.make_workload("llama3-8b", seed=0)
     c = w.cfg
