@@ -7,8 +7,8 @@ result run-to-run deterministic.  Covers both element types, both head
 widths, block sizes 8-64, group sizes that put 16, 4, 2 and 1 sequences in a
 work item (and a group split over two column chunks), a prefix that is not
 a whole number of partitions, a batch that is not a whole number of groups,
-sequences that end inside the prefix, invalid lengths, and the full
-shared-prefix batch at both block sizes."""
+sequences that end inside the prefix, invalid lengths, seeded random shapes,
+and the full shared-prefix batch at both block sizes."""
 
 import numpy as np
 import pytest
@@ -258,3 +258,34 @@ def test_paths_without_shared_items(pa, case):
     ref = oracle_out(w, k_ref, v_ref)
     err = np.abs(as_f64(out1) - ref)
     assert (err <= TOL[w.cfg.dtype] + rounding_bound(ref, w.cfg.dtype)).all()
+
+
+@pytest.mark.parametrize("seed", range(8))
+def test_random_shapes_against_oracle(pa, seed):
+    """Seeded random batches: batch size, group size, head width, block
+    size, partition size and prefix length all drawn, so the plan sees
+    shared items fewer than, equal to and more than the full partitions,
+    groups that do not divide the batch, and prefixes of zero to several
+    partitions."""
+    rng = np.random.default_rng(1000 + seed)
+    dtype = ["bf16", "f16"][seed % 2]
+    D = [64, 128][int(rng.integers(0, 2))]
+    BS = [8, 16, 32][int(rng.integers(0, 3))]
+    Hkv = int(rng.integers(1, 4))
+    G = int(rng.choice([1, 2, 3, 4, 6, 8, 16]))
+    P = BS * int(rng.integers(1, 9))
+    B = int(rng.integers(1, 60))
+    plen = BS * int(rng.integers(0, 30))
+    ctx = [plen + int(s) for s in rng.integers(1, 5 * P, size=B)]
+    w = wl.make_custom(ctx, n_q_heads=Hkv * G, n_kv_heads=Hkv, d_head=D,
+                       block_size=BS, dtype=dtype, seed=2000 + seed,
+                       prefix_len=plen)
+    d = DeviceBatch(w)
+    name = f"random seed {seed}: {dtype} D{D} BS{BS} Hkv{Hkv} G{G} B{B}"
+    out, _ = _run(pa, d, P, plen, write=True, name=name)
+    k_ref, v_ref = oracle_pools_after_write(w)
+    assert from_dev(d.k_pool).tobytes() == k_ref.tobytes()
+    ref = oracle_out(w, k_ref, v_ref)
+    err = np.abs(as_f64(out) - ref)
+    assert (err <= TOL[dtype] + rounding_bound(ref, dtype)).all(), \
+        (name, float(err.max()))
