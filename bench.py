@@ -6,7 +6,9 @@ Three forms are timed: "fused" (pa_decode_step -- the write folded into the
 partitioned attention -- then pa_reduce), "partitioned" (pa_cache_write,
 pa_decode_partitioned, pa_reduce) and "single" (pa_cache_write, the
 single-pass pa_decode); the line reports the fused step, the others' times
-beside it (--variant best reports the fastest instead).  Inputs are seeded
+beside it (--variant best reports the fastest instead).  A batch whose rows
+share a prompt's blocks also times "prefix" (pa_decode_shared_prefix with
+the write folded in, then pa_reduce) and reports that.  Inputs are seeded
 synthetic batches (see paged_kv_cache_222_amd/workloads.py); the default is
 the LLaMA-3-8B-shaped GQA batch (B=128, 32/8 heads, d128, bf16, log-normal
 context lengths).  Several copies of the inputs are resident in HBM and the
@@ -14,7 +16,8 @@ steps rotate over them, so no step finds the previous step's K/V in the
 256 MB last-level cache.
 
 Prints one JSON line: KV-read GB/s (value), seq-steps/s, fraction of the
-8 TB/s HBM peak, the dominant kernel's roofline figures from HIP events, and
+8 TB/s HBM peak, the dominant kernel's roofline figures from HIP events, the
+achievable read ceiling measured on the same device (pa_read_ceiling), and
 the fp64 CPU oracle timed on a bounded sample of the same batch.
 """
 
