@@ -16,8 +16,10 @@
  * Conventions for every entry point
  * ---------------------------------
  * - Pointers are DEVICE pointers owned by the caller unless stated otherwise.
- *   The GPU entry points never allocate, free or retain memory and keep no
- *   state between calls, so calls on different streams are independent.
+ *   The GPU entry points never allocate, free or retain memory.  The only
+ *   state they keep is a per-device note of how many work groups fit on the
+ *   device (filled on first use, thread-safe), so calls on different
+ *   streams or threads are independent.
  *   The host-side block pool (pa_pool_*, pa_block_hashes, at the end) works
  *   on HOST memory: a pool is an object the caller creates and destroys.
  * - All arrays are dense and row-major, with the shapes given below, and
@@ -163,7 +165,11 @@ int pa_decode(void* out, const void* q, const void* k_pool, const void* v_pool,
 /*
  * pa_decode_partitioned -- the same attention split along the context into
  * partitions of partition_size positions, each reduced to softmax statistics
- * that pa_reduce combines (log-sum-exp merge).  Partition p of sequence b
+ * that pa_reduce combines (log-sum-exp merge).  The pages do not describe
+ * this split: it is an exact rearrangement of the attention of pa_decode
+ * (rounding aside) that lets a long context, or a small batch, spread over
+ * the whole GPU; the decode it serves reads the whole cache and is bound by
+ * memory reads ("Serving", section 23.2).  Partition p of sequence b
  * covers positions [p * P, min((p + 1) * P, n)).  For each non-empty
  * partition and query head, with s_t as in pa_decode:
  *   max_logits[b, h, p] = m, a reference logit within 8 ln 2 below the
@@ -199,6 +205,9 @@ int pa_decode_partitioned(float* max_logits, float* exp_sums, float* tmp_out,
  * slots of positions n - 1 followed by pa_decode_partitioned, bit for bit,
  * in one launch: the work item that covers position n - 1 writes the row
  * and uses it directly.  fp32 runs the write as a separate kernel first.
+ * The write also happens for a sequence that needs more than max_partitions
+ * partitions (whose output pa_reduce reports as NaN), so a caller that
+ * retries with a larger workspace finds the token in the cache.
  *
  *   key_new, value_new [batch, n_kv_heads, d_head] dtype, read
  *   k_pool, v_pool     written at position n - 1 of each sequence, read
@@ -215,24 +224,34 @@ int pa_decode_step(float* max_logits, float* exp_sums, float* tmp_out,
 
 /*
  * pa_decode_shared_prefix -- pa_decode_partitioned (key_new == NULL) or
- * pa_decode_step (key_new != NULL) for a batch whose sequences share a
- * prefix, such as a long system prompt, through the same physical blocks
+ * pa_decode_step (key_new != NULL) for a batch whose sequences share the
+ * physical blocks of a common prefix, a shared prompt for instance
  * ("Serving", section 23.4: sequences with a common prefix can share its
  * blocks).  The workspace it writes is the one those calls define, read by
  * pa_reduce; the values differ from theirs only by rounding order.
  *
- * Precondition: positions [0, prefix_len) of every sequence map to the same
- * physical blocks (the first ceil(prefix_len / block_size) table entries
- * are equal in every row).  The first floor(prefix_len / partition_size)
- * partitions -- fewer if some sequence with a valid length (1..max_blocks *
- * block_size) ends in or before them -- are then computed for several
- * sequences in one work item: each K/V tile of the prefix is read once for
- * 16 / gqa_group sequences (at least one) instead of once per sequence.  If
- * the rows do not share those entries the result is attention over the
- * first row's prefix blocks for every sequence of the item; out-of-pool
- * block ids still give NaN, never an out-of-bounds read.  With batch >
- * 1024, fp32, or a device too small for one work group per KV head the call
- * is pa_decode_partitioned / pa_decode_step (prefix_len unused).
+ * Stated by the caller: positions [0, prefix_len) of every sequence map to
+ * the same physical blocks (the first ceil(prefix_len / block_size) table
+ * entries are equal in every row).  The first floor(prefix_len /
+ * partition_size) partitions -- fewer if some sequence with a valid length
+ * ends in or before them -- are then computed for several sequences in one
+ * work item: each K/V tile of the prefix is read once for 16 / gqa_group
+ * sequences (at least one) instead of once per sequence.
+ *
+ * Contract violations have defined results:
+ * - a sequence whose table entries for such a shared partition differ from
+ *   those of the first sequence of its work item gets NaN in every output
+ *   element (the item reads one table for all its sequences and checks the
+ *   others against it); out-of-pool block ids give NaN, never an
+ *   out-of-bounds read;
+ * - with key_new != NULL, a sequence whose new token would land inside the
+ *   shared positions (n - 1 < prefix_len, so the write would change a block
+ *   other sequences read) is not written and gets NaN in every output
+ *   element.  This holds on every path, including the fallbacks below.
+ * A valid length is one of 1 .. max_blocks * block_size that does not break
+ * the second rule.  With batch > 1024, fp32, or a device too small for one
+ * work group per KV head no work item is shared: the call computes what
+ * pa_decode_partitioned / pa_decode_step compute, with the second rule.
  *
  *   prefix_len >= 0 (PA_ERR_SHAPE otherwise)
  *   key_new, value_new  both NULL, or both [batch, n_kv_heads, d_head] dtype
@@ -282,7 +301,10 @@ int pa_decode_multi(float* max_logits, float* exp_sums, float* tmp_out,
                     float scale, int32_t dtype, void* stream);
 
 /*
- * pa_reduce -- merge per-partition statistics into the attention output.
+ * pa_reduce -- merge per-partition statistics into the attention output:
+ * the second half of the split of pa_decode_partitioned (not on the pages;
+ * an exact identity of softmax: each partition's weights are rescaled to a
+ * common maximum and the partial outputs averaged by their denominators).
  * With n_p = ceil(n / partition_size), M = max_{p<n_p} m_p and
  * w_p = l_p * exp(m_p - M):
  *   out[b, h, :] = sum_p w_p tmp_out[b, h, p, :] / sum_p w_p

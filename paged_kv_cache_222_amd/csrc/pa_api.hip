@@ -1,6 +1,7 @@
 // C ABI of libpa: argument checks, launch geometry, dispatch to the kernels.
 // Declarations and the full contract are in include/pa.h.
 #include <algorithm>
+#include <atomic>
 #include <limits.h>
 #include <stdio.h>
 #include <stdlib.h>
@@ -86,22 +87,34 @@ pa::AttnArgs attention_args(const void* q, const void* k_pool, const void* v_poo
   return a;
 }
 
-// Work groups of the matrix-core kernel that fit on the whole device, cached
-// per (device, dtype, d_head): an occupancy query per call would cost more
-// than a small decode step.
+// Work groups of the matrix-core kernel that fit on the whole device.  It
+// depends only on the device and the kernel, and an occupancy query per call
+// would cost more than a small decode step, so it is memoised per (device,
+// dtype, d_head) for devices 0 .. kMemoDevices - 1 in relaxed atomics
+// (concurrent first calls store the same value); other devices are queried
+// on every call.
+constexpr int kMemoDevices = 64;
+
+int query_slots(int dev, int32_t dtype, int32_t d_head) {
+  int cus = 0;
+  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+      cus < 1)
+    cus = 256;
+  return cus * pa::attention_mfma_occupancy(dtype, d_head);
+}
+
 int device_slots(int32_t dtype, int32_t d_head) {
-  static int cache[16][2][2];
+  static std::atomic<int> memo[kMemoDevices][2][2];
   int dev = 0;
-  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 16) dev = 0;
-  int& c = cache[dev][dtype == PA_F16 ? 0 : 1][d_head == 64 ? 0 : 1];
-  if (c == 0) {
-    int cus = 0;
-    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
-        cus < 1)
-      cus = 256;
-    c = cus * pa::attention_mfma_occupancy(dtype, d_head);
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0) dev = 0;
+  if (dev >= kMemoDevices) return query_slots(dev, dtype, d_head);
+  std::atomic<int>& c = memo[dev][dtype == PA_F16 ? 0 : 1][d_head == 64 ? 0 : 1];
+  int v = c.load(std::memory_order_relaxed);
+  if (v == 0) {
+    v = query_slots(dev, dtype, d_head);
+    c.store(v, std::memory_order_relaxed);
   }
-  return c;
+  return v;
 }
 
 // fp16/bf16 run on the matrix cores (query heads in chunks of 16); fp32 on
@@ -182,6 +195,8 @@ int decode_partitioned(float* max_logits, float* exp_sums, float* tmp_out,
   a.n_queries = n_queries;
   if (prefix_len < 0) return PA_ERR_SHAPE;
   a.prefix_parts = prefix_len / partition_size;
+  // a folded write must not land in the shared positions (contract check)
+  a.shared_len = key_new ? prefix_len : 0;
   const int64_t rows = (int64_t)max_partitions * batch;
   if (rows * n_kv_heads * (((int64_t)gqa_group * n_queries + 7) / 8) > INT_MAX)
     return PA_ERR_SHAPE;
@@ -202,6 +217,7 @@ int decode_partitioned(float* max_logits, float* exp_sums, float* tmp_out,
       w.row_bytes = d_head * elem_bytes(dtype);
       w.block_shift = block_shift_of(block_size);
       w.n_blocks = n_blocks;
+      w.shared_len = prefix_len;
       const hipError_t e = pa::launch_append(w, (hipStream_t)stream);
       if (e != hipSuccess) return launch_status(e);
     } else {

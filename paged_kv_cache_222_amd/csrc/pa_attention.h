@@ -81,16 +81,18 @@ __global__ __launch_bounds__(kAttnThreads) void attention_kernel(AttnArgs a) {
   const int Hq = a.n_kv_heads * G;
   const int h0 = kvh * G + hc * GC;
   const int gv = min(GC, G - hc * GC);
-  const bool bad_ctx = ctx < 0 || (int64_t)ctx > ((int64_t)a.max_blocks << a.block_shift);
+  // invalid length, or a new token written into the shared positions
+  const bool bad_ctx = ctx < 0 || (int64_t)ctx > ((int64_t)a.max_blocks << a.block_shift) ||
+                       (ctx >= 1 && ctx - 1 < a.shared_len);
 
   int t0 = 0, t1 = ctx, p = 0;
   if (parts) {
     const int P = a.partition_size;
     const int64_t np64 = ctx > 0 ? ((int64_t)ctx + P - 1) / P : 0;
-    if (np64 > a.max_partitions) return;  // pa_reduce reports NaN
+    // np > max_partitions (and ctx < 0) are reported as NaN by pa_reduce;
+    // the fp32 step's cache write is a kernel of its own and still happens.
+    if (np64 > a.max_partitions) return;
     const int np = (int)np64;
-    // np > max_partitions (and ctx < 0) are reported as NaN by pa_reduce.
-    if (np > a.max_partitions) return;
     // Rows are dispatched in order; row j holds partition np - PMAX + j, so
     // the last rows carry every sequence's final (partial) partition and the
     // dispatcher fills the tail of the launch with the smallest items.

@@ -110,6 +110,17 @@ struct Mfma<Dt::F16> {
 // loop, including copies into the other buffer.  The kernel orders the
 // copies with explicit vmcnt waits instead; lds_wait() then waits for these
 // reads and ties their results to the wait, so no use is scheduled earlier.
+//
+// Why this is safe although the compiler takes an asm output as written the
+// moment the asm statement issues (the hardware writes it only when the LDS
+// read returns): every call site issues a group of these reads and then, in
+// the same basic block with nothing in between, the lds_wait() that names
+// every one of their destinations as a read-write operand.  So (1) each
+// destination stays live, and is not handed to another value, until the
+// wait; (2) no instruction reads a destination before the wait, since its
+// only use before then is the wait itself; (3) the volatile statements keep
+// their order.  A read whose destination is not passed to the wait that
+// follows it, or any code placed between the reads and the wait, breaks this.
 template <int OFF>
 __device__ __forceinline__ u32x4 lds_read_b128(uint32_t addr) {
   u32x4 r;
@@ -209,8 +220,9 @@ __global__ __launch_bounds__(kAttnThreads, PA_MFMA_MIN_BLOCKS) void attention_mf
   __shared__ float s_l[NW][16];
   __shared__ int s_bad[NW];
   // Shared-prefix launches: bit b set if sequence b's context length is
-  // invalid (negative or longer than its table); its columns of a shared
-  // item are written as NaN.
+  // invalid (negative or longer than its table, or its new token would be
+  // written into the shared positions); its columns of a shared item are
+  // written as NaN.
   __shared__ uint32_t s_inval[kPlanBatch / 32];
   // Partitioned plan: exclusive prefix of the full partitions per sequence
   // (and the total), then the sequences in the order their final partitions
@@ -269,7 +281,8 @@ __global__ __launch_bounds__(kAttnThreads, PA_MFMA_MIN_BLOCKS) void attention_mf
       int cmin = INT32_MAX;
 #pragma unroll
       for (int j = 0; j < 4; ++j)
-        if (cs[j] >= 1 && (int64_t)cs[j] <= max_ctx) cmin = min(cmin, cs[j]);
+        if (cs[j] >= 1 && (int64_t)cs[j] <= max_ctx && cs[j] - 1 >= a.shared_len)
+          cmin = min(cmin, cs[j]);
 #pragma unroll
       for (int d = 1; d < kWave; d <<= 1) cmin = min(cmin, shfl_xor_i(cmin, d));
       if (lane == 0) s_bad[wave] = cmin;
@@ -284,7 +297,8 @@ __global__ __launch_bounds__(kAttnThreads, PA_MFMA_MIN_BLOCKS) void attention_mf
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
         const int b = threadIdx.x * 4 + j;
-        if (b < B && (cs[j] < 0 || (int64_t)cs[j] > max_ctx))
+        if (b < B && (cs[j] < 0 || (int64_t)cs[j] > max_ctx ||
+                      (cs[j] >= 1 && cs[j] - 1 < a.shared_len)))
           atomicOr(&s_inval[b >> 5], 1u << (b & 31));
       }
     }
@@ -462,7 +476,10 @@ __global__ __launch_bounds__(kAttnThreads, PA_MFMA_MIN_BLOCKS) void attention_mf
     // a shared-prefix item's partition lies before every sequence's end
     const int ctx = pre ? (p + 1) * P
                         : ((const __attribute__((address_space(4))) int32_t*)a.context_lens)[b];
-    const bool bad_ctx = ctx < 0 || (int64_t)ctx > max_ctx;
+    // an invalid length, or (a folded write into a batch with shared
+    // positions) a new token that would land in a shared block
+    const bool bad_ctx = ctx < 0 || (int64_t)ctx > max_ctx ||
+                         (!pre && ctx >= 1 && ctx - 1 < a.shared_len);
     // columns per head of the group: query tokens, or a prefix item's sequences
     const int nq = pre ? a.prefix_seqs : NQ;
     const int nq_valid = pre ? min(nq, a.batch - bseq) : NQ;
@@ -479,14 +496,34 @@ __global__ __launch_bounds__(kAttnThreads, PA_MFMA_MIN_BLOCKS) void attention_mf
       t0 = p * P;
     } else if (parts) {
       const int64_t np = ctx > 0 ? ((int64_t)ctx + P - 1) / P : 0;
+      if (np > a.max_partitions) {
+        // The workspace cannot hold this sequence: no attention (pa_reduce
+        // reports NaN), but the folded cache write still happens, done by
+        // the item that would hold the final partition -- the last row of
+        // the grid, or the plan's tail item of the sequence.
+        // (The plan caps a sequence at max_partitions + 1 partitions, so its
+        // tail item has p == max_partitions.)
+        const bool writer = plan ? p == a.max_partitions
+                                 : rr / a.batch == a.max_partitions - 1;
+        if (a.key_new != nullptr && writer && !bad_ctx && wave == 0 && lane < CPR) {
+          const int tn = ctx - 1;
+          const int pblk = a.block_table[(int64_t)b * a.max_blocks + (tn >> a.block_shift)];
+          if (pblk >= 0 && pblk < a.n_blocks) {
+            const int64_t head_bytes = (int64_t)bs * RB;
+            const int64_t src = (int64_t)(b * a.n_kv_heads + kvh) * RB + lane * 16;
+            const int64_t dst = ((int64_t)pblk * a.n_kv_heads + kvh) * head_bytes +
+                                (int64_t)(tn & (bs - 1)) * RB + lane * 16;
+            *(u32x4*)((char*)a.k_pool + dst) = *(const u32x4*)((const char*)a.key_new + src);
+            *(u32x4*)((char*)a.v_pool + dst) = *(const u32x4*)((const char*)a.value_new + src);
+          }
+        }
+        continue;
+      }
       if (!plan) {
         // one work group per (row, sequence): row j holds partition
         // np - PMAX + j, so final partitions are dispatched last
-        if (np > a.max_partitions) continue;  // pa_reduce reports NaN
         p = (int)np - a.max_partitions + rr / a.batch;
         if (p < 0) continue;
-      } else if (np > a.max_partitions) {
-        continue;
       }
       if (bad_ctx) {
         for (int idx = threadIdx.x; idx < gv * D; idx += kAttnThreads) {
@@ -550,6 +587,11 @@ __global__ __launch_bounds__(kAttnThreads, PA_MFMA_MIN_BLOCKS) void attention_mf
                                                            (int64_t)bseq * a.max_blocks);
     char* my_ring = s_ring + wave * 4 * TILE;  // slot x: K at 2x*TILE, V at (2x+1)*TILE
     bool bad = false;
+    // A shared item reads the first sequence's table for the whole group:
+    // bit s is set when sequence bseq + s names other blocks for a tile of
+    // the item (the rows do not share the prefix as stated), and that
+    // sequence's columns are written as NaN.
+    uint32_t mis = 0u;
 
     // Byte offsets (in a KV head's view of a pool) of a tile's rows 0-7 and
     // rows 8-15 (row r lives at base + r * RB).  With blocks of 16 or more
@@ -570,6 +612,12 @@ __global__ __launch_bounds__(kAttnThreads, PA_MFMA_MIN_BLOCKS) void attention_mf
       const bool ok0 = p0 >= 0 && p0 < a.n_blocks;
       const bool ok1 = p1 >= 0 && p1 < a.n_blocks;
       bad |= !(ok0 && ok1);
+      if (pre) {
+        for (int sq = 1; sq < nq_valid; ++sq) {
+          const __attribute__((address_space(4))) int32_t* orow = trow + (int64_t)sq * a.max_blocks;
+          if (orow[bl0] != p0 || orow[bl1] != p1) mis |= 1u << sq;
+        }
+      }
       TileBase t;
       t.lo = (ok0 ? (int64_t)p0 : 0) * blk_bytes + (int64_t)(tok & (bs - 1)) * RB;
       t.hi = (ok1 ? (int64_t)p1 : 0) * blk_bytes + (int64_t)(tok_hi & (bs - 1)) * RB - 8 * RB;
@@ -748,7 +796,7 @@ __global__ __launch_bounds__(kAttnThreads, PA_MFMA_MIN_BLOCKS) void attention_mf
       s_m[wave][lane] = m;
       s_l[wave][lane] = lh;
     }
-    if (lane == 0) s_bad[wave] = bad ? 1 : 0;
+    if (lane == 0) s_bad[wave] = (int)(mis | (bad ? 1u : 0u));  // mis never has bit 0
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       const int h = lg * 4 + j;
@@ -759,8 +807,12 @@ __global__ __launch_bounds__(kAttnThreads, PA_MFMA_MIN_BLOCKS) void attention_mf
     }
     lds_barrier();
     bool anybad = false;
+    uint32_t allmis = 0u;
 #pragma unroll
-    for (int w = 0; w < NW; ++w) anybad |= s_bad[w] != 0;
+    for (int w = 0; w < NW; ++w) {
+      anybad |= (s_bad[w] & 1) != 0;
+      allmis |= (uint32_t)s_bad[w] & ~1u;
+    }
     // Thread (column g, dims d..d+3) of pass j: 4 outputs per thread, so a
     // 16-column chunk takes NP passes of the work group.  Every LDS read of
     // the merge comes before its first store: the compiler orders reads of
@@ -778,8 +830,10 @@ __global__ __launch_bounds__(kAttnThreads, PA_MFMA_MIN_BLOCKS) void attention_mf
       if (idx < gv * D4) {
         const int g = idx / D4, d = (idx - g * D4) * 4;
         if (pre) {
-          const int sb = bseq + (c0 + g) / G;
+          const int sq = (c0 + g) / G;
+          const int sb = bseq + sq;
           colbad[j] |= ((s_inval[sb >> 5] >> (sb & 31)) & 1u) != 0u;
+          colbad[j] |= ((allmis >> sq) & 1u) != 0u;
         }
 #pragma unroll
         for (int w = 0; w < NW; ++w) {

@@ -36,8 +36,9 @@ __global__ __launch_bounds__(kWriteThreads) void cache_write_kernel(CacheWriteAr
 }
 
 // The same copy with the slot taken from the block table: each sequence's
-// new row goes to position context_lens[b] - 1 (a sequence with no position
-// or whose table entry lies outside the pool is skipped).
+// new row goes to position context_lens[b] - 1 (a sequence with no position,
+// whose table entry lies outside the pool, or whose new position lies in the
+// shared positions [0, shared_len) is skipped).
 __global__ __launch_bounds__(kWriteThreads) void append_kernel(AppendArgs a) {
   const int cpr = a.row_bytes >> 4;
   const int64_t per_seq = (int64_t)a.n_kv_heads * cpr;
@@ -50,6 +51,7 @@ __global__ __launch_bounds__(kWriteThreads) void append_kernel(AppendArgs a) {
   const int ctx = a.context_lens[b];
   if (ctx < 1 || (int64_t)ctx > ((int64_t)a.max_blocks << a.block_shift)) return;
   const int pos = ctx - 1;
+  if (pos < a.shared_len) return;
   const int blk = a.block_table[(int64_t)b * a.max_blocks + (pos >> a.block_shift)];
   if (blk < 0 || blk >= a.n_blocks) return;
   const int off = pos & ((1 << a.block_shift) - 1);

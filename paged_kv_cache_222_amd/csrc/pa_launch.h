@@ -44,6 +44,11 @@ struct AttnArgs {
   // sequences at once (columns = (sequence, head) pairs).  0: off.
   int32_t prefix_parts;
   int32_t prefix_seqs;
+  // With a folded write into a batch whose positions [0, shared_len) sit in
+  // blocks every row shares: a sequence whose new token falls there would
+  // write into a shared block, so it is a contract violation -- no write,
+  // NaN outputs.  0: no such positions.
+  int32_t shared_len;
   float scale_log2;    // scale * log2(e)
 };
 
@@ -85,6 +90,7 @@ struct AppendArgs {
   int32_t row_bytes;
   int32_t block_shift;
   int32_t n_blocks;
+  int32_t shared_len;   // as in AttnArgs: a new token before it is not written
 };
 
 constexpr int kCopyThreads = 256;

@@ -12,7 +12,7 @@ import torch
 
 import oracle
 from helpers import (TOL, TORCH_DT, as_f64, from_dev, note,
-                     oracle_pools_after_write, rounding_bound, to_dev)
+                     oracle_pools_after_write, out_bound, to_dev)
 from paged_kv_cache_222_amd import workloads as wl
 
 pytestmark = pytest.mark.gpu
@@ -67,7 +67,7 @@ def test_multi_query_small(pa, dtype, D, BS, Hkv, G, k, P):
                                      w.context_lens, w.scale, c.gqa_group,
                                      c.block_size, c.dtype)
     got = as_f64(out)
-    bound = TOL[dtype] + rounding_bound(ref, dtype)
+    bound = out_bound(ref, dtype)
     err = np.abs(got - ref)
     print(f"{dtype} D{D} BS{BS} G{G} k{k} P{P}: max err {err.max():.3g}")
     assert (err <= bound).all()
