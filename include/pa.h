@@ -385,6 +385,47 @@ int pa_pool_release(pa_block_pool* pool, const int32_t* ids, int32_t n);
 int pa_pool_map_prefix(pa_block_pool* pool, const uint64_t* hashes, int32_t n,
                        int32_t* ids, int32_t* n_hit);
 
+/*
+ * pa_pool_simulate -- requests growing token by token in a pool of n_blocks
+ * blocks of block_size tokens, under one of two policies: the contrast of
+ * the widget of "Serving" section 23.4 (a 96-block pool and eight requests:
+ * reserving each request's worst case lets four run at once, paging lets
+ * every request start when it arrives) and of the utilisation figures in
+ * the "Paged Attention" summary on the inference-serving tag page.  Blocks
+ * are real ids drawn from and returned to a pa_block_pool.
+ *
+ * Request i arrives at step arrivals[i] holding prompt_lens[i] tokens.  At
+ * each step: arrived requests join a queue in arrival order (ties by index);
+ * the head of the queue starts while the blocks it needs are free --
+ *   PA_SIM_RESERVE: ceil(max_len / block_size) blocks, held to the end;
+ *   PA_SIM_PAGED:   ceil(prompt / block_size) blocks, one more each time its
+ *                   tokens pass the blocks it holds;
+ * then the step is counted (running[step] = requests running; the step's
+ * stored tokens and held capacity, blocks * block_size, are added to
+ * *util_tokens and *util_capacity); then each running request finishes if
+ * it holds final_lens[i] tokens (finish[i] = step, its blocks freed) or
+ * gains one token.  The simulation ends after the step in which the last
+ * request finishes; *n_steps = that step + 1.  Utilisation is
+ * *util_tokens / *util_capacity.
+ *
+ *   arrivals, prompt_lens, final_lens [n_requests] int32, host, read
+ *   start, finish [n_requests] int32, host, written
+ *   running [max_steps] int32, host, written (the first min(n_steps,
+ *           max_steps) entries)
+ * Errors: PA_ERR_SHAPE for a negative arrival, a prompt < 1, a final length
+ * below the prompt (or above max_len when reserving), or a trace longer than
+ * max_steps (the other outputs are still complete); PA_ERR_NOSPACE if some
+ * request needs more blocks than the pool has to start, or (paging) the
+ * pool runs out while requests grow.
+ */
+enum { PA_SIM_RESERVE = 0, PA_SIM_PAGED = 1 };
+int pa_pool_simulate(const int32_t* arrivals, const int32_t* prompt_lens,
+                     const int32_t* final_lens, int32_t n_requests,
+                     int32_t n_blocks, int32_t block_size, int32_t policy,
+                     int32_t max_len, int32_t* start, int32_t* finish,
+                     int32_t* running, int32_t max_steps, int32_t* n_steps,
+                     int64_t* util_tokens, int64_t* util_capacity);
+
 /* Static text for a status code; never NULL. */
 const char* pa_strerror(int status);
 

@@ -7,11 +7,12 @@ path, and sharing no code with it.
 
 What it follows:
 
-* Paging ("Serving", §23.4 Paged Attention): the cache lives in fixed-size
-  blocks handed out as a sequence grows; sequences sharing a prefix can share
-  its blocks.  The §23.4 widget: a pool of 96 blocks serving eight requests
-  that arrive over time and grow token by token; reserving each request's
-  maximum lets only four run, paging lets every request run on arrival.
+* Paging ("Serving", §23.4 Paged Attention): cache memory is handed out in
+  fixed-size blocks as sequences grow, and a block can be shared by the
+  sequences whose prefix it holds.  The section's widget contrasts the two
+  policies on a 96-block pool and eight requests arriving over time: with
+  worst-case reservations four requests at most hold blocks at once, while
+  with paging none of them waits.
 * Prefix caching by block hashes (the prompt-caching articles on the
   pagedattention tag page): a full block is named by a hash of its tokens
   chained with the previous block's hash, so reuse needs an identical prefix
@@ -133,68 +134,69 @@ class OraclePool:
         return ids, hit
 
 
+def _ceil_div(a: int, b: int) -> int:
+    return -(-a // b)
+
+
 def simulate(arrivals, prompt_lens, final_lens, n_blocks, block_size,
              policy, max_len=None):
-    """Requests in a pool of ``n_blocks`` blocks of ``block_size`` tokens.
+    """Requests in a pool of ``n_blocks`` blocks of ``block_size`` tokens,
+    worked out from each request's timeline rather than step by step.
 
     Request i arrives at step ``arrivals[i]`` with ``prompt_lens[i]`` tokens
-    and gains one token per step while it runs, until it holds
-    ``final_lens[i]`` tokens; then it finishes and frees its blocks.  Waiting
-    requests start in arrival order as soon as they fit:
+    and, once started at step s_i, holds ``prompt_lens[i] + (t - s_i)``
+    tokens at step t until it holds ``final_lens[i]``: it finishes at
+    f_i = s_i + final_lens[i] - prompt_lens[i] and frees its blocks after
+    that step is counted.  Blocks held at step t ("Serving", section 23.4:
+    paging hands out blocks as a sequence grows; reserving takes the worst
+    case up front):
 
-    * ``"reserve"``: a request holds ceil(max_len / block_size) blocks from
-      start to finish (its worst case, in one piece);
-    * ``"paged"``: a request holds ceil(tokens / block_size) blocks, taking a
-      new block when its tokens cross a block boundary.
+    * ``"reserve"``: ceil(max_len / block_size) for every step of its life;
+    * ``"paged"``: ceil(tokens(t) / block_size).
 
-    Returns per-request start and finish steps, the number running at every
-    step, and the mean utilisation (tokens stored / token capacity of the
-    blocks held)."""
+    Start steps follow from one recurrence on the free blocks: requests
+    start in arrival order (ties by index); request i starts at the first
+    step t >= arrivals[i], not before the request ahead of it, at which its
+    first step's blocks fit in n_blocks minus the blocks held at t by the
+    requests already started with s_j <= t <= f_j.  Utilisation sums, over
+    every step and running request, the tokens stored and the capacity of
+    the blocks held (blocks * block_size).  Raises RuntimeError when a
+    request could never start or the paged pool would overflow."""
     n = len(arrivals)
-    cap = [0] * n                 # blocks held
-    tokens = [0] * n
+    bs = block_size
+    life = [final_lens[i] - prompt_lens[i] for i in range(n)]
+
+    def held(i, s, t):
+        if policy == "reserve":
+            return _ceil_div(max_len, bs)
+        return _ceil_div(prompt_lens[i] + (t - s), bs)
+
+    order = sorted(range(n), key=lambda i: (arrivals[i], i))
     start = [None] * n
-    finish = [None] * n
-    free = n_blocks
-    running, waiting = [], []
-    step = 0
-    trace = []
-    util_num = util_den = 0
-    need_res = -(-max_len // block_size) if max_len else None
-    while any(f is None for f in finish):
-        for i in range(n):
-            if arrivals[i] == step:
-                waiting.append(i)
-        # start waiting requests in arrival order while they fit
-        while waiting:
-            i = waiting[0]
-            need = need_res if policy == "reserve" else -(-prompt_lens[i] // block_size)
-            if need > free:
+    t = 0
+    for k, i in enumerate(order):
+        need = held(i, 0, 0)
+        if need > n_blocks:
+            raise RuntimeError("a request needs more blocks than the pool has")
+        t = max(t, arrivals[i])
+        while True:
+            in_use = sum(held(j, start[j], t) for j in order[:k]
+                         if start[j] <= t <= start[j] + life[j])
+            if need <= n_blocks - in_use:
                 break
-            waiting.pop(0)
-            free -= need
-            cap[i] = need
-            tokens[i] = prompt_lens[i]
-            start[i] = step
-            running.append(i)
-        trace.append(len(running))
-        for i in running:
-            util_num += tokens[i]
-            util_den += cap[i] * block_size
-        # every running request gains a token (or finishes)
-        for i in list(running):
-            if tokens[i] >= final_lens[i]:
-                finish[i] = step
-                free += cap[i]
-                cap[i] = 0
-                running.remove(i)
-                continue
-            tokens[i] += 1
-            if policy == "paged" and tokens[i] > cap[i] * block_size:
-                if free == 0:
-                    raise RuntimeError("pool exhausted")
-                free -= 1
-                cap[i] += 1
-        step += 1
-    return {"start": start, "finish": finish, "running": trace,
-            "utilisation": util_num / util_den if util_den else 0.0}
+            t += 1
+        start[i] = t
+    finish = [start[i] + life[i] for i in range(n)]
+    n_steps = max(finish) + 1 if n else 0
+    running, tok, cap = [], 0, 0
+    for t in range(n_steps):
+        live = [i for i in range(n) if start[i] <= t <= finish[i]]
+        blocks = sum(held(i, start[i], t) for i in live)
+        if blocks > n_blocks:
+            raise RuntimeError("the pool runs out while requests grow")
+        running.append(len(live))
+        tok += sum(prompt_lens[i] + (t - start[i]) for i in live)
+        cap += blocks * bs
+    return {"start": start, "finish": finish, "running": running,
+            "tokens": tok, "capacity": cap,
+            "utilisation": tok / cap if cap else 0.0}

@@ -29,6 +29,7 @@ from ._binding import (  # noqa: F401
     pa_pool_map_prefix,
     pa_pool_refcount,
     pa_pool_release,
+    pa_pool_simulate,
     pa_read_ceiling,
     pa_reduce,
     pa_strerror,

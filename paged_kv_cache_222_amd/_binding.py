@@ -25,6 +25,7 @@ _lock = threading.Lock()
 PA_OK, PA_ERR_NULL, PA_ERR_SHAPE, PA_ERR_UNSUPPORTED = 0, -1, -2, -3
 PA_ERR_WORKSPACE, PA_ERR_PARTITION, PA_ERR_HIP, PA_ERR_ALIGN = -4, -5, -6, -7
 PA_ERR_NOSPACE = -8
+PA_SIM_RESERVE, PA_SIM_PAGED = 0, 1
 
 
 class PaError(RuntimeError):
@@ -106,6 +107,11 @@ def load() -> ctypes.CDLL:
             getattr(lib, fn).restype = ctypes.c_int
         lib.pa_pool_map_prefix.argtypes = [vp, u64p, i32, i32p, i32p]
         lib.pa_pool_map_prefix.restype = ctypes.c_int
+        i64p = ctypes.POINTER(ctypes.c_int64)
+        lib.pa_pool_simulate.argtypes = [i32p, i32p, i32p, i32, i32, i32, i32,
+                                         i32, i32p, i32p, i32p, i32, i32p,
+                                         i64p, i64p]
+        lib.pa_pool_simulate.restype = ctypes.c_int
         lib.pa_strerror.argtypes = [ctypes.c_int]
         lib.pa_strerror.restype = ctypes.c_char_p
         _lib = lib
@@ -530,3 +536,40 @@ def pa_pool_map_prefix(pool: BlockPool, hashes):
         pool.handle, h.ctypes.data_as(ctypes.POINTER(ctypes.c_uint64)),
         len(h), _i32p(ids), ctypes.byref(hit)))
     return ids[:len(h)], hit.value
+
+
+def pa_pool_simulate(arrivals, prompt_lens, final_lens, n_blocks: int,
+                     block_size: int, policy: str, max_len: int = 0):
+    """Run the native pool simulation (see include/pa.h); returns a dict
+    with per-request ``start``/``finish`` steps, ``running`` (requests
+    running at each step), ``tokens``/``capacity`` (the utilisation sums)
+    and ``utilisation``.  ``policy`` is "reserve" or "paged"."""
+    import numpy as np
+    codes = {"reserve": PA_SIM_RESERVE, "paged": PA_SIM_PAGED}
+    if policy not in codes:
+        raise ValueError(f"unknown policy {policy!r}")
+    lib = load()
+    a = np.ascontiguousarray(arrivals, dtype=np.int32)
+    pr = np.ascontiguousarray(prompt_lens, dtype=np.int32)
+    fi = np.ascontiguousarray(final_lens, dtype=np.int32)
+    n = len(a)
+    if len(pr) != n or len(fi) != n:
+        raise ValueError("arrivals, prompt_lens and final_lens differ in length")
+    # every request runs at most final - prompt + 1 steps after the last
+    # arrival before it, so this many steps always suffice
+    max_steps = int(a.max(initial=0)) + int((fi.astype(np.int64) -
+                                             pr + 1).sum()) + 1
+    start = np.zeros(max(1, n), dtype=np.int32)
+    finish = np.zeros(max(1, n), dtype=np.int32)
+    running = np.zeros(max_steps, dtype=np.int32)
+    steps = ctypes.c_int32(0)
+    tok, cap = ctypes.c_int64(0), ctypes.c_int64(0)
+    _check("pa_pool_simulate", lib.pa_pool_simulate(
+        _i32p(a), _i32p(pr), _i32p(fi), n, int(n_blocks), int(block_size),
+        codes[policy], int(max_len or 0), _i32p(start), _i32p(finish),
+        _i32p(running), max_steps, ctypes.byref(steps), ctypes.byref(tok),
+        ctypes.byref(cap)))
+    return {"start": start[:n].tolist(), "finish": finish[:n].tolist(),
+            "running": running[:steps.value].tolist(),
+            "tokens": tok.value, "capacity": cap.value,
+            "utilisation": tok.value / cap.value if cap.value else 0.0}

@@ -15,7 +15,9 @@
 //  * a block whose reference count drops to zero is free; if it carries a
 //    hash it stays findable by that hash until it is reused.
 #include <cstdint>
+#include <algorithm>
 #include <cstring>
+#include <deque>
 #include <map>
 #include <new>
 #include <set>
@@ -203,6 +205,95 @@ int pa_pool_map_prefix(pa_block_pool* pool, const uint64_t* hashes, int32_t n, i
   }
   *n_hit = hit;
   return PA_OK;
+}
+
+int pa_pool_simulate(const int32_t* arrivals, const int32_t* prompt_lens,
+                     const int32_t* final_lens, int32_t n_requests, int32_t n_blocks,
+                     int32_t block_size, int32_t policy, int32_t max_len, int32_t* start,
+                     int32_t* finish, int32_t* running, int32_t max_steps, int32_t* n_steps,
+                     int64_t* util_tokens, int64_t* util_capacity) {
+  if (!n_steps || !util_tokens || !util_capacity) return PA_ERR_NULL;
+  if (n_requests < 0 || n_blocks < 1 || block_size < 1 || max_steps < 0) return PA_ERR_SHAPE;
+  if (policy != PA_SIM_RESERVE && policy != PA_SIM_PAGED) return PA_ERR_SHAPE;
+  if (n_requests > 0 && (!arrivals || !prompt_lens || !final_lens || !start || !finish))
+    return PA_ERR_NULL;
+  if (max_steps > 0 && !running) return PA_ERR_NULL;
+  const int32_t reserve = policy == PA_SIM_RESERVE ? (max_len + block_size - 1) / block_size : 0;
+  for (int32_t i = 0; i < n_requests; ++i) {
+    if (arrivals[i] < 0 || prompt_lens[i] < 1 || final_lens[i] < prompt_lens[i])
+      return PA_ERR_SHAPE;
+    if (policy == PA_SIM_RESERVE && final_lens[i] > max_len) return PA_ERR_SHAPE;
+    const int32_t need =
+        policy == PA_SIM_RESERVE ? reserve : (prompt_lens[i] + block_size - 1) / block_size;
+    if (need > n_blocks) return PA_ERR_NOSPACE;  // could never start
+  }
+  pa_block_pool* pool = pa_pool_create(n_blocks);
+  if (!pool) return PA_ERR_NOSPACE;
+  // requests in arrival order (ties by index): the order waiting requests start in
+  std::vector<int32_t> order(n_requests);
+  for (int32_t i = 0; i < n_requests; ++i) order[i] = i;
+  std::stable_sort(order.begin(), order.end(),
+                   [&](int32_t x, int32_t y) { return arrivals[x] < arrivals[y]; });
+  std::vector<std::vector<int32_t>> held(n_requests);
+  std::vector<int32_t> tokens(n_requests, 0);
+  std::vector<int32_t> live;    // running requests, in start order
+  std::deque<int32_t> waiting;  // arrived, not started
+  int32_t next = 0, done = 0, step = 0, status = PA_OK;
+  int64_t tok_sum = 0, cap_sum = 0;
+  for (int32_t i = 0; i < n_requests; ++i) start[i] = finish[i] = -1;
+  while (done < n_requests) {
+    while (next < n_requests && arrivals[order[next]] == step) waiting.push_back(order[next++]);
+    // start waiting requests in arrival order while their blocks are free
+    while (!waiting.empty()) {
+      const int32_t i = waiting.front();
+      const int32_t need =
+          policy == PA_SIM_RESERVE ? reserve : (prompt_lens[i] + block_size - 1) / block_size;
+      if (need > pool->available()) break;
+      waiting.pop_front();
+      held[i].resize(need);
+      pa_pool_alloc(pool, need, held[i].data());
+      tokens[i] = prompt_lens[i];
+      start[i] = step;
+      live.push_back(i);
+    }
+    if (step < max_steps) running[step] = (int32_t)live.size();
+    for (int32_t i : live) {
+      tok_sum += tokens[i];
+      cap_sum += (int64_t)held[i].size() * block_size;
+    }
+    // each running request finishes, or gains a token (and a block when its
+    // tokens pass the blocks it holds)
+    std::vector<int32_t> still;
+    still.reserve(live.size());
+    for (int32_t i : live) {
+      if (tokens[i] >= final_lens[i]) {
+        finish[i] = step;
+        pa_pool_release(pool, held[i].data(), (int32_t)held[i].size());
+        held[i].clear();
+        ++done;
+        continue;
+      }
+      ++tokens[i];
+      if (policy == PA_SIM_PAGED && (int64_t)tokens[i] > (int64_t)held[i].size() * block_size) {
+        int32_t b;
+        if (pa_pool_alloc(pool, 1, &b) != PA_OK) {
+          status = PA_ERR_NOSPACE;  // the pool ran out while requests grew
+          break;
+        }
+        held[i].push_back(b);
+      }
+      still.push_back(i);
+    }
+    if (status != PA_OK) break;
+    live.swap(still);
+    ++step;
+  }
+  pa_pool_destroy(pool);
+  *n_steps = step;
+  *util_tokens = tok_sum;
+  *util_capacity = cap_sum;
+  if (status == PA_OK && step > max_steps) status = PA_ERR_SHAPE;  // trace cut short
+  return status;
 }
 
 }  // extern "C"

@@ -34,7 +34,8 @@ def test_header_declares_the_entry_points():
          "pa_decode_shared_prefix", "pa_decode_step", "pa_pool_alloc",
          "pa_pool_available", "pa_pool_create", "pa_pool_destroy",
          "pa_pool_fork", "pa_pool_map_prefix", "pa_pool_refcount",
-         "pa_pool_release", "pa_read_ceiling", "pa_reduce", "pa_strerror"])
+         "pa_pool_release", "pa_pool_simulate", "pa_read_ceiling",
+         "pa_reduce", "pa_strerror"])
 
 
 def test_library_exports_every_declared_symbol(lib):
