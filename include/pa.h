@@ -72,7 +72,9 @@ enum {
   PA_ERR_PARTITION = -5,   /* partition_size not a positive multiple of block_size */
   PA_ERR_HIP = -6,         /* the HIP runtime reported an error at launch */
   PA_ERR_ALIGN = -7,       /* an array pointer is not 16-byte aligned */
-  PA_ERR_NOSPACE = -8      /* the block pool has too few free blocks */
+  PA_ERR_NOSPACE = -8,     /* the block pool has too few free blocks */
+  PA_ERR_SCRATCH = -9      /* pa_decode_step_noalloc: the workspace would not
+                              fit the fixed scratch buffer */
 };
 
 /*
@@ -221,6 +223,38 @@ int pa_decode_step(float* max_logits, float* exp_sums, float* tmp_out,
                    int32_t batch, int32_t n_kv_heads, int32_t gqa_group,
                    int32_t d_head, int32_t block_size, int32_t n_blocks,
                    float scale, int32_t dtype, void* stream);
+
+/*
+ * pa_decode_step_noalloc -- pa_decode_step followed by pa_reduce, with the
+ * partition workspace in a fixed buffer inside the library instead of
+ * caller memory: for callers that cannot allocate device memory (code under
+ * HIP graph capture, tight serving loops, harnesses that forbid allocation).
+ * It allocates and frees nothing.
+ *
+ * max_partitions is ceil(max_blocks * block_size / partition_size), enough
+ * for any valid context; the workspace is n_q_heads * batch *
+ * max_partitions * (d_head + 2) * 4 bytes and must fit the buffer's
+ * 32 MiB (PA_ERR_SCRATCH otherwise, nothing enqueued): e.g. the LLaMA-3-8B
+ * batch (B 128, 32 query heads, d 128, 8192-position tables) at partition
+ * 3072 needs 6.4 MB.  The buffer is one per GPU, kept until the process
+ * ends; every call on a GPU uses the same one, so calls that overlap on one
+ * GPU (different streams or threads) race.  Nothing in it needs to start
+ * at zero: every entry pa_reduce reads is first written by the attention.
+ * The result -- pools and out -- is bit-identical to pa_decode_step +
+ * pa_reduce with that max_partitions.
+ *
+ *   out            [batch, n_kv_heads * gqa_group, d_head] dtype, written
+ *   Other arguments as in pa_decode_step.
+ */
+int pa_decode_step_noalloc(void* out, int32_t partition_size,
+                           const void* key_new, const void* value_new,
+                           const void* q, void* k_pool, void* v_pool,
+                           const int32_t* block_table, int32_t max_blocks,
+                           const int32_t* context_lens, int32_t batch,
+                           int32_t n_kv_heads, int32_t gqa_group,
+                           int32_t d_head, int32_t block_size,
+                           int32_t n_blocks, float scale, int32_t dtype,
+                           void* stream);
 
 /*
  * pa_decode_shared_prefix -- pa_decode_partitioned (key_new == NULL) or

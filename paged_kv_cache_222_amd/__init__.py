@@ -21,6 +21,7 @@ from ._binding import (  # noqa: F401
     pa_decode_partitioned,
     pa_decode_shared_prefix,
     pa_decode_step,
+    pa_decode_step_noalloc,
     pa_pool_alloc,
     pa_pool_available,
     pa_pool_create,

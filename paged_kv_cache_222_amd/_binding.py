@@ -24,7 +24,7 @@ _lock = threading.Lock()
 # status codes of include/pa.h
 PA_OK, PA_ERR_NULL, PA_ERR_SHAPE, PA_ERR_UNSUPPORTED = 0, -1, -2, -3
 PA_ERR_WORKSPACE, PA_ERR_PARTITION, PA_ERR_HIP, PA_ERR_ALIGN = -4, -5, -6, -7
-PA_ERR_NOSPACE = -8
+PA_ERR_NOSPACE, PA_ERR_SCRATCH = -8, -9
 PA_SIM_RESERVE, PA_SIM_PAGED = 0, 1
 
 
@@ -73,6 +73,9 @@ def load() -> ctypes.CDLL:
                                                 vp, vp, vp, vp, i32, vp, i32,
                                                 i32, i32, i32, i32, i32, i32,
                                                 f32, i32, vp]
+        lib.pa_decode_step_noalloc.argtypes = [vp, i32, vp, vp, vp, vp, vp,
+                                               vp, i32, vp, i32, i32, i32,
+                                               i32, i32, i32, f32, i32, vp]
         lib.pa_read_ceiling.argtypes = [vp, ctypes.c_int64, vp, ctypes.c_int64,
                                         i32, vp, vp]
         lib.pa_decode.argtypes = [vp, vp, vp, vp, vp, i32, vp, i32, i32, i32,
@@ -84,7 +87,8 @@ def load() -> ctypes.CDLL:
                                   i32, vp]
         for fn in ("pa_cache_write", "pa_copy_blocks", "pa_decode",
                    "pa_decode_partitioned", "pa_decode_multi", "pa_decode_step",
-                   "pa_decode_shared_prefix", "pa_reduce", "pa_read_ceiling"):
+                   "pa_decode_shared_prefix", "pa_decode_step_noalloc",
+                   "pa_reduce", "pa_read_ceiling"):
             getattr(lib, fn).restype = ctypes.c_int
         u64p = ctypes.POINTER(ctypes.c_uint64)
         i32p = ctypes.POINTER(ctypes.c_int32)
@@ -308,6 +312,30 @@ def pa_decode_step(max_logits, exp_sums, tmp_out, key_new, value_new, q,
         q.data_ptr(), k_pool.data_ptr(), v_pool.data_ptr(),
         block_table.data_ptr(), mb, context_lens.data_ptr(), B, n_kv, G, d, bs,
         n_blocks, float(scale), _dtype_code(q), _stream(stream)))
+
+
+def pa_decode_step_noalloc(out, key_new, value_new, q, k_pool, v_pool,
+                           block_table, context_lens, *, partition_size, scale,
+                           stream=None):
+    """pa_decode_step + pa_reduce into out [B, Hq, D] with the partition
+    workspace in the library's fixed scratch buffer (no device allocation;
+    PaError with PA_ERR_SCRATCH when it would not fit)."""
+    lib = load()
+    B, Hq, n_kv, G, d, bs, n_blocks, mb = _attention_common(
+        q, k_pool, v_pool, block_table, context_lens)
+    _dev("out", out, q.dtype, 3)
+    if tuple(out.shape) != tuple(q.shape):
+        raise ValueError("out must have q's shape")
+    _dev("key_new", key_new, q.dtype, 3)
+    _dev("value_new", value_new, q.dtype, 3)
+    if tuple(key_new.shape) != (B, n_kv, d) or value_new.shape != key_new.shape:
+        raise ValueError("key_new/value_new must be [B, n_kv_heads, d_head]")
+    _check("pa_decode_step_noalloc", lib.pa_decode_step_noalloc(
+        out.data_ptr(), int(partition_size), key_new.data_ptr(),
+        value_new.data_ptr(), q.data_ptr(), k_pool.data_ptr(),
+        v_pool.data_ptr(), block_table.data_ptr(), mb, context_lens.data_ptr(),
+        B, n_kv, G, d, bs, n_blocks, float(scale), _dtype_code(q),
+        _stream(stream)))
 
 
 def pa_decode_shared_prefix(max_logits, exp_sums, tmp_out, q, k_pool, v_pool,

@@ -230,6 +230,32 @@ int decode_partitioned(float* max_logits, float* exp_sums, float* tmp_out,
   return st2 != PA_OK ? st2 : launch_status(e);
 }
 
+// The fixed workspace of pa_decode_step_noalloc: one array per GPU the
+// library runs on, held until the process ends.  In host code `scratch`
+// names a host-side stand-in, not device memory: its device address comes
+// from hipGetSymbolAddress, once per device (with that device current), and
+// only that address is handed to kernels.  Calls that overlap on one GPU
+// share the array and race.
+constexpr int64_t kScratchBytes = int64_t(32) << 20;
+__device__ __align__(256) char scratch[kScratchBytes];
+
+// Device address of `scratch` on the current device, memoised for devices
+// 0 .. kMemoDevices - 1 (concurrent first calls store the same address);
+// null if the runtime cannot give it.
+void* scratch_address() {
+  static std::atomic<void*> memo[kMemoDevices];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0) return nullptr;
+  if (dev < kMemoDevices) {
+    void* p = memo[dev].load(std::memory_order_relaxed);
+    if (p) return p;
+  }
+  void* p = nullptr;
+  if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess) return nullptr;
+  if (dev < kMemoDevices && p) memo[dev].store(p, std::memory_order_relaxed);
+  return p;
+}
+
 }  // namespace
 
 extern "C" {
@@ -245,6 +271,8 @@ const char* pa_strerror(int status) {
     case PA_ERR_HIP: return "the HIP runtime reported an error at kernel launch";
     case PA_ERR_ALIGN: return "an array pointer is not 16-byte aligned";
     case PA_ERR_NOSPACE: return "the block pool has too few free blocks";
+    case PA_ERR_SCRATCH:
+      return "the partition workspace would exceed the library's fixed 32 MiB scratch buffer";
     default: return "unknown status";
   }
 }
@@ -434,6 +462,43 @@ int pa_reduce(void* out, const float* max_logits, const float* exp_sums,
   a.max_partitions = max_partitions;
   (void)hipGetLastError();
   return launch_status(pa::launch_reduce(a, dtype, d_head, (hipStream_t)stream));
+}
+
+int pa_decode_step_noalloc(void* out, int32_t partition_size, const void* key_new,
+                           const void* value_new, const void* q, void* k_pool, void* v_pool,
+                           const int32_t* block_table, int32_t max_blocks,
+                           const int32_t* context_lens, int32_t batch, int32_t n_kv_heads,
+                           int32_t gqa_group, int32_t d_head, int32_t block_size,
+                           int32_t n_blocks, float scale, int32_t dtype, void* stream) {
+  if (batch < 0) return PA_ERR_SHAPE;
+  if (batch == 0) return PA_OK;
+  if (!out || !key_new || !value_new) return PA_ERR_NULL;
+  // every host-side check before the first HIP call
+  const int st0 = check_attention(q, k_pool, v_pool, block_table, max_blocks, context_lens,
+                                  batch, n_kv_heads, gqa_group, d_head, block_size, n_blocks,
+                                  dtype);
+  if (st0 != PA_OK) return st0;
+  if (partition_size <= 0 || partition_size % block_size != 0) return PA_ERR_PARTITION;
+  if (!aligned16(out) || !aligned16(key_new) || !aligned16(value_new)) return PA_ERR_ALIGN;
+  // enough partitions for the longest context the table can hold
+  const int64_t pmax = ((int64_t)max_blocks * block_size + partition_size - 1) / partition_size;
+  const int64_t rows = (int64_t)batch * n_kv_heads * gqa_group;
+  const int64_t bytes = rows * pmax * (d_head + 2) * 4;
+  if (bytes > kScratchBytes) return PA_ERR_SCRATCH;
+  void* base = scratch_address();
+  if (!base) return PA_ERR_HIP;
+  float* tmp_out = static_cast<float*>(base);       // [rows, pmax, d_head]
+  float* max_logits = tmp_out + rows * pmax * d_head;  // [rows, pmax]
+  float* exp_sums = max_logits + rows * pmax;           // [rows, pmax]
+  // every workspace entry pa_reduce reads is written first by the attention
+  // launch, so nothing needs clearing between calls
+  const int st = pa_decode_step(max_logits, exp_sums, tmp_out, partition_size, (int32_t)pmax,
+                                key_new, value_new, q, k_pool, v_pool, block_table, max_blocks,
+                                context_lens, batch, n_kv_heads, gqa_group, d_head, block_size,
+                                n_blocks, scale, dtype, stream);
+  if (st != PA_OK) return st;
+  return pa_reduce(out, max_logits, exp_sums, tmp_out, context_lens, batch,
+                   n_kv_heads * gqa_group, d_head, partition_size, (int32_t)pmax, dtype, stream);
 }
 
 }  // extern "C"

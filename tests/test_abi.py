@@ -15,7 +15,7 @@ HEADER = os.path.join(ROOT, "include", "pa.h")
 
 PA_OK, PA_ERR_NULL, PA_ERR_SHAPE, PA_ERR_UNSUPPORTED = 0, -1, -2, -3
 PA_ERR_WORKSPACE, PA_ERR_PARTITION, PA_ERR_HIP, PA_ERR_ALIGN = -4, -5, -6, -7
-PA_ERR_NOSPACE = -8
+PA_ERR_NOSPACE, PA_ERR_SCRATCH = -8, -9
 
 P = 0x100000        # a fake, 16-byte aligned device address (never touched)
 MIS = P + 8         # misaligned
@@ -31,7 +31,8 @@ def test_header_declares_the_entry_points():
     assert declared_functions() == sorted(
         ["pa_block_hashes", "pa_cache_write", "pa_copy_blocks", "pa_decode",
          "pa_decode_multi", "pa_decode_partitioned",
-         "pa_decode_shared_prefix", "pa_decode_step", "pa_pool_alloc",
+         "pa_decode_shared_prefix", "pa_decode_step",
+         "pa_decode_step_noalloc", "pa_pool_alloc",
          "pa_pool_available", "pa_pool_create", "pa_pool_destroy",
          "pa_pool_fork", "pa_pool_map_prefix", "pa_pool_refcount",
          "pa_pool_release", "pa_pool_simulate", "pa_read_ceiling",
@@ -53,11 +54,11 @@ def test_strerror_covers_every_status(lib):
     seen = set()
     for st in (PA_OK, PA_ERR_NULL, PA_ERR_SHAPE, PA_ERR_UNSUPPORTED,
                PA_ERR_WORKSPACE, PA_ERR_PARTITION, PA_ERR_HIP, PA_ERR_ALIGN,
-               PA_ERR_NOSPACE):
+               PA_ERR_NOSPACE, PA_ERR_SCRATCH):
         text = lib.pa_strerror(st).decode()
         assert text and text != "unknown status"
         seen.add(text)
-    assert len(seen) == 9
+    assert len(seen) == 10
     assert lib.pa_strerror(12345).decode() == "unknown status"
 
 
@@ -201,6 +202,36 @@ def test_step_argument_checks(lib):
     assert _step(lib, kn=MIS) == PA_ERR_ALIGN
     assert _step(lib, psz=8) == PA_ERR_PARTITION
     assert _step(lib, d=32) == PA_ERR_UNSUPPORTED
+
+
+def _noalloc(lib, **kw):
+    a = dict(out=P, psz=512, kn=P, vn=P, q=P, k=P, v=P, tbl=P, mb=64, ctx=P,
+             B=4, hkv=2, G=4, d=128, bs=16, nb=32, scale=0.1, dt=2)
+    a.update(kw)
+    return lib.pa_decode_step_noalloc(
+        a["out"], a["psz"], a["kn"], a["vn"], a["q"], a["k"], a["v"],
+        a["tbl"], a["mb"], a["ctx"], a["B"], a["hkv"], a["G"], a["d"],
+        a["bs"], a["nb"], a["scale"], a["dt"], None)
+
+
+def test_noalloc_argument_checks(lib):
+    """Every refusal comes before any HIP call (so these run without a
+    GPU), the fixed buffer's limit included."""
+    assert _noalloc(lib, B=0) == PA_OK
+    for k in ("out", "kn", "vn", "q", "k", "v", "tbl", "ctx"):
+        assert _noalloc(lib, **{k: None}) == PA_ERR_NULL, k
+    assert _noalloc(lib, out=MIS) == PA_ERR_ALIGN
+    assert _noalloc(lib, kn=MIS) == PA_ERR_ALIGN
+    assert _noalloc(lib, psz=8) == PA_ERR_PARTITION
+    assert _noalloc(lib, d=32) == PA_ERR_UNSUPPORTED
+    assert _noalloc(lib, B=-1) == PA_ERR_SHAPE
+    # 256 x 32 heads x ceil(8192 / 512) partitions x 130 floats = 68 MB
+    assert _noalloc(lib, B=256, hkv=8, mb=512, psz=512) == PA_ERR_SCRATCH
+    # exactly at the limit: 32 MiB = rows * pmax * 130 * 4 has no integer
+    # solution, so check one row below and above it
+    rows_fit = (32 << 20) // (130 * 4)               # with pmax = 1
+    assert _noalloc(lib, B=rows_fit + 1, hkv=1, G=1, mb=32, psz=512) == \
+        PA_ERR_SCRATCH
 
 
 def _prefix(lib, **kw):
