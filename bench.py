@@ -2,23 +2,28 @@
 
 A step is the whole hot path over one batch: the cache write of each
 sequence's new token, then attention over every sequence's paged cache.
-Three forms are timed: "fused" (pa_decode_step -- the write folded into the
-partitioned attention -- then pa_reduce), "partitioned" (pa_cache_write,
-pa_decode_partitioned, pa_reduce) and "single" (pa_cache_write, the
-single-pass pa_decode); the line reports the fused step, the others' times
-beside it (--variant best reports the fastest instead).  A batch whose rows
-share a prompt's blocks also times "prefix" (pa_decode_shared_prefix with
-the write folded in, then pa_reduce) and reports that.  Inputs are seeded
-synthetic batches (see paged_kv_cache_222_amd/workloads.py); the default is
-the LLaMA-3-8B-shaped GQA batch (B=128, 32/8 heads, d128, bf16, log-normal
-context lengths).  Several copies of the inputs are resident in HBM and the
-steps rotate over them, so no step finds the previous step's K/V in the
-256 MB last-level cache.
+Four forms are timed: "fused" (pa_decode_step -- the write folded into the
+partitioned attention -- then pa_reduce), "split" (pa_decode_split: the
+context cut into pieces of equal runs of tiles, the write folded in, then
+pa_reduce), "partitioned" (pa_cache_write, pa_decode_partitioned,
+pa_reduce) and "single" (pa_cache_write, the single-pass pa_decode); the
+line reports the batch's headline form (see HEADLINE_FORM), the others'
+times beside it (--variant best reports the fastest instead).  A batch
+whose rows share a prompt's blocks also times "prefix"
+(pa_decode_shared_prefix with the write folded in, then pa_reduce) and
+reports that.  Inputs are seeded synthetic batches (see
+paged_kv_cache_222_amd/workloads.py); the default is the LLaMA-3-8B-shaped
+GQA batch (B=128, 32/8 heads, d128, bf16, log-normal context lengths).
+Several copies of the inputs are resident in HBM and the steps rotate over
+them, so no step finds the previous step's K/V in the 256 MB last-level
+cache.
 
 Prints one JSON line: KV-read GB/s (value), seq-steps/s, fraction of the
-8 TB/s HBM peak, the dominant kernel's roofline figures from HIP events, the
-achievable read ceiling measured on the same device (pa_read_ceiling), and
-the fp64 CPU oracle timed on a bounded sample of the same batch.
+8 TB/s HBM peak, the dominant kernel's roofline figures -- its duration from
+the timestamps of its own dispatch, recorded in HIP events on the stream it
+runs on (pa_time_next_attention) -- the achievable read ceiling measured on
+the same device (pa_read_ceiling), and the fp64 CPU oracle timed on a
+bounded sample of the same batch.
 """
 
 from __future__ import annotations
@@ -54,12 +59,16 @@ def parse():
     ap.add_argument("--partition-size", type=int, default=None)
     ap.add_argument("--copies", type=int, default=3,
                     help="resident input copies the steps rotate over")
-    ap.add_argument("--variant", choices=["all", "best", "fused",
+    ap.add_argument("--variant", choices=["all", "best", "fused", "split",
                                           "partitioned", "single", "prefix"],
                     default="all",
                     help="all (default): time every form, report the fused "
                          "step (the shared-prefix step for a batch with a "
                          "shared prefix); best: report the fastest form")
+    ap.add_argument("--slots", type=int, default=None,
+                    help="split form: workspace slots per row (default: the "
+                         "fewest that let every work group take an even "
+                         "share, from the batch's lengths and the device)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-read-ceiling", action="store_true",
                     help="skip the read-ceiling calibration (pa_read_ceiling "
@@ -97,6 +106,12 @@ def algorithmic_bytes(w):
     tbl = 4 * int((-(-w.context_lens.astype(np.int64) // c.block_size)).sum())
     return kv + q + tbl + 4 * c.batch
 
+
+# The form each batch's line reports by default (--variant all): the fastest
+# form measured on MI355X for that batch (a batch with a shared prefix
+# reports "prefix").
+HEADLINE_FORM = {"llama3-8b": "fused", "qwen2.5-1.5b": "split",
+                 "llama2-7b": "fused", "tiny": "fused"}
 
 # sources whose change invalidates the HBM byte counts stored under profiles/
 KERNEL_SOURCES = ["pa_attention_mfma.h", "pa_attention_mfma.hip",
@@ -142,12 +157,29 @@ def measured_traffic(name, variant, P, block_size):
         return None
 
 
-def measure_read_ceiling(torch, pa, gib=4, reps=10):
+def split_slots(w, torch):
+    """Workspace slots for pa_decode_split: the fewest that let every work
+    group take an even share of the tiles.  A column (KV head and chunk of
+    16 query columns) has 2 * CUs / columns work groups (two per CU fit);
+    its even share is R = ceil(tiles / work groups) tiles, and a sequence of
+    T tiles is cut into at most ceil(T / R) + 1 pieces."""
+    c = w.cfg
+    cols = c.n_kv_heads * -(-c.gqa_group // 16)
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    wg = max(1, (2 * cus) // cols)
+    tiles = -(-w.context_lens.astype(np.int64) // 16)
+    share = -(-int(tiles.sum()) // wg)
+    return int(max(2, min(16, -(-int(tiles.max()) // share) + 1)))
+
+
+def measure_read_ceiling(torch, pa, gib=4, reps=10, batch_tiles=0):
     """The device's achievable HBM read rate for the attention kernels'
     access pattern: pa_read_ceiling over a ``gib`` GiB buffer, in address
     order and as a gather of its 4 KiB tiles in a random order (median of
     ``reps`` launches timed with HIP events on torch's current stream, the
-    stream the launches go to)."""
+    stream the launches go to).  With ``batch_tiles``, also the gather of
+    only that many tiles -- as many bytes as one decode step reads -- whose
+    rate includes the start and end of a launch of that size."""
     nbytes = gib << 30
     buf = torch.zeros(nbytes // 4, dtype=torch.int32, device="cuda")
     n_tiles = nbytes // 4096
@@ -155,7 +187,11 @@ def measure_read_ceiling(torch, pa, gib=4, reps=10):
     order = torch.randperm(n_tiles, generator=gen).to(torch.int32).cuda()
     sink = torch.zeros(1, dtype=torch.int32, device="cuda")
     res = {"buffer_bytes": nbytes, "tile_bytes": 4096}
-    for name, kw in (("stream", {}), ("tile_gather", {"tile_order": order})):
+    legs = [("stream", {}), ("tile_gather", {"tile_order": order})]
+    if batch_tiles:
+        legs.append(("batch_size_tile_gather",
+                     {"tile_order": order, "n_tiles": int(batch_tiles)}))
+    for name, kw in legs:
         for _ in range(2):
             pa.pa_read_ceiling(buf, sink, **kw)
         torch.cuda.synchronize()
@@ -168,7 +204,11 @@ def measure_read_ceiling(torch, pa, gib=4, reps=10):
             torch.cuda.synchronize()
             ts.append(e0.elapsed_time(e1))
         ms = float(np.median(ts))
-        res[f"{name}_GBs"] = round(nbytes / (ms * 1e-3) / 1e9, 1)
+        moved = nbytes if "n_tiles" not in kw else kw["n_tiles"] * 4096
+        res[f"{name}_GBs"] = round(moved / (ms * 1e-3) / 1e9, 1)
+        if "n_tiles" in kw:
+            res[f"{name}_bytes"] = moved
+            res[f"{name}_us"] = round(ms * 1e3, 2)
     del buf, order
     torch.cuda.empty_cache()
     return res
@@ -303,6 +343,7 @@ def bench_verify(args, torch, pa, wl):
         pa.pa_cache_write(x["kn"], x["vn"], x["k"], x["v"], slots)
         if ev is not None:
             ev[1].record(stream)
+            pa.pa_time_next_attention(ev[4], ev[5])
         pa.pa_decode_multi(*ws, x["q"], x["k"], x["v"], tbl, cl,
                            partition_size=P, scale=w.scale)
         if ev is not None:
@@ -319,16 +360,19 @@ def bench_verify(args, torch, pa, wl):
         step(copies[i % len(copies)])
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)]
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(6)]
            for _ in range(args.steps)]
     for i in range(args.steps):
         step(copies[i % len(copies)], evs[i])
     torch.cuda.synchronize()
+    # write, attention call, reduce call, attention kernel (its own
+    # timestamps), microseconds
     per = np.array([[e[0].elapsed_time(e[1]), e[1].elapsed_time(e[2]),
-                     e[2].elapsed_time(e[3])] for e in evs]) * 1e3
+                     e[2].elapsed_time(e[3]), e[4].elapsed_time(e[5])]
+                    for e in evs]) * 1e3
     ms = wall / args.steps * 1e3
     kv = w.kv_bytes_logical()
-    attn_us = float(per[:, 1].mean())
+    attn_us = float(per[:, 3].mean())
     nb = 2
     alg = kv + B * k * Hq * D * nb + 4 * int(
         (-(-w.context_lens.astype(np.int64) // c.block_size)).sum()) + 4 * B
@@ -572,20 +616,31 @@ def main():
     tbl, cl, slots = up(w.block_table), up(w.context_lens), up(w.slot_mapping)
     out = torch.empty_like(copies[0]["q"])
     ws = pa.partition_workspace(c.batch, c.n_q_heads, c.d_head, pmax)
+    n_slots = args.slots or split_slots(w, torch)
+    ws_split = pa.partition_workspace(c.batch, c.n_q_heads, c.d_head, n_slots)
     torch.cuda.synchronize()
     stream = torch.cuda.current_stream()
 
     def step(x, variant, ev=None):
+        """One decode step; with ``ev`` (six events) it records the step's
+        start, the end of the separate write, the ends of the attention and
+        the reduce calls, and -- through pa_time_next_attention -- the
+        attention kernel's own start and end."""
         if ev is not None:
             ev[0].record(stream)
-        if variant in ("fused", "prefix"):
+        if variant in ("fused", "prefix", "split"):
             # the cache write happens inside the attention launch
             if ev is not None:
                 ev[1].record(stream)
+                pa.pa_time_next_attention(ev[4], ev[5])
             if variant == "fused":
                 pa.pa_decode_step(*ws, x["kn"], x["vn"], x["q"], x["k"],
                                   x["v"], tbl, cl, partition_size=P,
                                   scale=w.scale)
+            elif variant == "split":
+                pa.pa_decode_split(*ws_split, x["q"], x["k"], x["v"], tbl, cl,
+                                   scale=w.scale, key_new=x["kn"],
+                                   value_new=x["vn"])
             else:
                 # the shared prompt's partitions computed for several
                 # sequences per work item
@@ -595,13 +650,17 @@ def main():
                     key_new=x["kn"], value_new=x["vn"])
             if ev is not None:
                 ev[2].record(stream)
-            pa.pa_reduce(out, *ws, cl, partition_size=P)
+            if variant == "split":
+                pa.pa_reduce(out, *ws_split, cl, partition_size=0)
+            else:
+                pa.pa_reduce(out, *ws, cl, partition_size=P)
             if ev is not None:
                 ev[3].record(stream)
             return
         pa.pa_cache_write(x["kn"], x["vn"], x["k"], x["v"], slots)
         if ev is not None:
             ev[1].record(stream)
+            pa.pa_time_next_attention(ev[4], ev[5])
         if variant == "single":
             pa.pa_decode(out, x["q"], x["k"], x["v"], tbl, cl, scale=w.scale)
             if ev is not None:
@@ -626,20 +685,25 @@ def main():
         torch.cuda.synchronize()
         wall = time.perf_counter() - t0
         # the same steps again with events around each kernel
-        evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)]
+        evs = [[torch.cuda.Event(enable_timing=True) for _ in range(6)]
                for _ in range(args.steps)]
         for i in range(args.steps):
             step(copies[i % len(copies)], variant, evs[i])
         torch.cuda.synchronize()
+        # microseconds: write, attention call, reduce call, whole step, and
+        # the attention kernel itself (its dispatch's own timestamps)
         per = np.array([[e[0].elapsed_time(e[1]), e[1].elapsed_time(e[2]),
-                         e[2].elapsed_time(e[3]), e[0].elapsed_time(e[3])]
-                        for e in evs]) * 1e3   # microseconds
+                         e[2].elapsed_time(e[3]), e[0].elapsed_time(e[3]),
+                         e[4].elapsed_time(e[5])]
+                        for e in evs]) * 1e3
         return wall, per
 
-    variants = (["fused", "partitioned", "single"]
+    variants = (["fused", "split", "partitioned", "single"]
                 if args.variant in ("all", "best") else [args.variant])
     if c.prefix_len and args.variant in ("all", "best"):
         variants.insert(0, "prefix")
+    if c.dtype == "f32" and "split" in variants and args.variant != "split":
+        variants.remove("split")            # 16-bit types only
     if args.variant == "prefix" and not c.prefix_len:
         sys.exit("--variant prefix needs a batch with a shared prefix")
     results = {}
@@ -647,10 +711,10 @@ def main():
         log(f"timing {v}: warmup {args.warmup}, steps {args.steps}")
         wall, per = timed(v)
         results[v] = (wall, per)
-        log(f"{v}: {wall / args.steps * 1e3:.4f} ms/step wall; kernel us "
-            f"write {per[:, 0].mean():.1f} attn {per[:, 1].mean():.1f} "
-            f"reduce {per[:, 2].mean():.1f}")
-    headline = "prefix" if c.prefix_len else "fused"
+        log(f"{v}: {wall / args.steps * 1e3:.4f} ms/step wall; us: write "
+            f"{per[:, 0].mean():.1f} attention call {per[:, 1].mean():.1f} "
+            f"(kernel {per[:, 4].mean():.1f}) reduce {per[:, 2].mean():.1f}")
+    headline = "prefix" if c.prefix_len else HEADLINE_FORM.get(c.name, "fused")
     best = (min(results, key=lambda v: results[v][0]) if args.variant == "best"
             else headline if args.variant == "all" else args.variant)
     wall, per = results[best]
@@ -658,15 +722,16 @@ def main():
     kv = w.kv_bytes_logical()
     uniq = w.kv_bytes_unique() if c.prefix_len else kv
     gbs = kv / (ms * 1e-3) / 1e9
-    attn_us = float(per[:, 1].mean())
+    attn_us = float(per[:, 4].mean())      # the kernel's own timestamps
     alg = algorithmic_bytes(w)
     if c.prefix_len:
         alg = alg - kv + uniq
-    if best in ("fused", "prefix"):   # the new rows are read and written by the same launch
+    if best in ("fused", "prefix", "split"):   # the new rows are read and written by the same launch
         alg += 2 * 2 * c.batch * c.n_kv_heads * c.d_head * \
             {"f32": 4, "f16": 2, "bf16": 2}[c.dtype]
     achieved = alg / (attn_us * 1e-6) / 1e9
     kernel = {"fused": "attention_mfma_kernel (pa_decode_step)",
+              "split": "attention_mfma_kernel (pa_decode_split)",
               "prefix": "attention_mfma_kernel (pa_decode_shared_prefix)",
               "partitioned": "attention_mfma_kernel (pa_decode_partitioned)",
               "single": "attention_mfma_kernel (pa_decode)"}[best]
@@ -689,14 +754,17 @@ def main():
                    "n_kv_heads": c.n_kv_heads, "d_head": c.d_head,
                    "block_size": c.block_size, "partition_size": P,
                    "sum_context": int(w.context_lens.sum()),
-                   "seed": args.seed, "variant": best},
+                   "seed": args.seed, "variant": best,
+                   "split_slots": n_slots if best == "split" else None},
         "seq_steps_per_s": round(c.batch / (ms * 1e-3), 1),
         "pct_of_hbm_peak": round(100 * (uniq / (ms * 1e-3) / 1e9)
                                  / HBM_PEAK_GBS, 2),
         "kv_bytes_per_step": kv,
         "kv_bytes_unique_per_step": uniq,
-        "kernel_us": {"cache_write": round(float(per[:, 0].mean()), 2),
+        "kernel_us": {"cache_write": (None if best in ("fused", "prefix", "split")
+                                      else round(float(per[:, 0].mean()), 2)),
                       "attention": round(attn_us, 2),
+                      "attention_call_events": round(float(per[:, 1].mean()), 2),
                       "reduce": round(float(per[:, 2].mean()), 2),
                       "step_events": round(float(per[:, 3].mean()), 2),
                       "step_events_p10_p50_p90": [
@@ -724,9 +792,11 @@ def main():
     if not args.no_read_ceiling:
         log("measuring the read ceiling (4 GiB, stream and 4 KiB-tile gather)")
         del copies
-        rc = measure_read_ceiling(torch, pa)
+        rc = measure_read_ceiling(torch, pa, batch_tiles=uniq // 4096)
         rc["attention_frac_of_tile_gather"] = round(
             achieved / rc["tile_gather_GBs"], 4)
+        rc["attention_frac_of_batch_size_gather"] = round(
+            achieved / rc["batch_size_tile_gather_GBs"], 4)
         rec["read_ceiling"] = rc
     if not args.no_cpu_baseline:
         log("timing the fp64 CPU oracle on a sample")

@@ -142,6 +142,19 @@ int pa_read_ceiling(const void* buf, int64_t buf_bytes, const int32_t* tile_orde
                     void* stream);
 
 /*
+ * pa_time_next_attention -- a measurement aid, not part of the decode path:
+ * the attention kernel launched next by a decode call on this thread (any
+ * of pa_decode, pa_decode_partitioned, pa_decode_step, pa_decode_split,
+ * pa_decode_shared_prefix, pa_decode_multi) records its own start in
+ * start_event and its end in stop_event (hipEvent_t handles the caller
+ * created with timing enabled; either may be NULL).  hipEventElapsedTime
+ * of the two is then the kernel's execution time, without the gaps between
+ * launches that events recorded around the call also measure.  The events
+ * are consumed by that one launch; NULL, NULL cancels.  Host-side only.
+ */
+int pa_time_next_attention(void* start_event, void* stop_event);
+
+/*
  * pa_decode -- one query token per sequence attends over all its cached
  * positions, in one pass per (sequence, KV head).
  *
@@ -304,6 +317,43 @@ int pa_decode_shared_prefix(float* max_logits, float* exp_sums, float* tmp_out,
                             int32_t dtype, void* stream);
 
 /*
+ * pa_decode_split -- the decode step (the write of pa_decode_step when
+ * key_new != NULL, none when NULL) with the context cut into pieces by
+ * work rather than by position, for batches whose lengths are uneven or
+ * too few to fill the GPU evenly with fixed partitions.  Like the
+ * partition split, this is not on the pages: an exact rearrangement of the
+ * attention of pa_decode (rounding aside); the decode reads the whole cache
+ * and is bound by memory reads ("Serving", section 23.2), so the work is
+ * what each part reads.
+ *
+ * All sequences' 16-position tiles, in sequence order, are cut into equal
+ * runs, one run per work group; a sequence is cut where a run ends.  Slot j
+ * of a row holds the statistics of the sequence's j-th piece (positions in
+ * order): max_logits, exp_sums and tmp_out as pa_decode_partitioned
+ * defines them for a partition, over the piece's positions.  Slots past the
+ * sequence's last piece get exp_sums = 0 (and max_logits = -inf; tmp_out is
+ * not written).  No sequence is cut into more than max_partitions pieces
+ * (the runs are lengthened if needed), so max_partitions >= 2 is the only
+ * requirement (PA_ERR_WORKSPACE otherwise); more slots allow a more even
+ * split.  pa_reduce with partition_size = 0 merges the pieces.  A
+ * sequence with an invalid length gets NaN in every slot.  fp16 and bf16
+ * only (PA_ERR_UNSUPPORTED for fp32).
+ *
+ *   max_logits, exp_sums [batch, n_q_heads, max_partitions] float32, written
+ *   tmp_out   [batch, n_q_heads, max_partitions, d_head]     float32, written
+ *   key_new, value_new  both NULL, or both [batch, n_kv_heads, d_head]
+ *   Other arguments as in pa_decode_step.
+ */
+int pa_decode_split(float* max_logits, float* exp_sums, float* tmp_out,
+                    int32_t max_partitions, const void* key_new,
+                    const void* value_new, const void* q, void* k_pool,
+                    void* v_pool, const int32_t* block_table,
+                    int32_t max_blocks, const int32_t* context_lens,
+                    int32_t batch, int32_t n_kv_heads, int32_t gqa_group,
+                    int32_t d_head, int32_t block_size, int32_t n_blocks,
+                    float scale, int32_t dtype, void* stream);
+
+/*
  * pa_decode_multi -- several query tokens per sequence: the last n_queries
  * positions of each sequence, causal among themselves, as in the one pass
  * in which the target model checks all drafted tokens of speculative
@@ -343,7 +393,10 @@ int pa_decode_multi(float* max_logits, float* exp_sums, float* tmp_out,
  * w_p = l_p * exp(m_p - M):
  *   out[b, h, :] = sum_p w_p tmp_out[b, h, p, :] / sum_p w_p
  * n == 0 gives a zero row (and so does a row whose partitions all have
- * exp_sums = 0).  Arrays as in pa_decode_partitioned; out as in pa_decode.
+ * exp_sums = 0).  A partition with exp_sums = 0 adds nothing and its
+ * tmp_out is not read.  partition_size = 0 merges a pa_decode_split
+ * workspace: every slot (pieces, not partitions) of rows with n >= 1.
+ * Arrays as in pa_decode_partitioned; out as in pa_decode.
  */
 int pa_reduce(void* out, const float* max_logits, const float* exp_sums,
               const float* tmp_out, const int32_t* context_lens, int32_t batch,

@@ -20,6 +20,7 @@ from ._binding import (  # noqa: F401
     pa_decode_multi,
     pa_decode_partitioned,
     pa_decode_shared_prefix,
+    pa_decode_split,
     pa_decode_step,
     pa_decode_step_noalloc,
     pa_pool_alloc,
@@ -34,5 +35,6 @@ from ._binding import (  # noqa: F401
     pa_read_ceiling,
     pa_reduce,
     pa_strerror,
+    pa_time_next_attention,
     partition_workspace,
 )

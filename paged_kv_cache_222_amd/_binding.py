@@ -73,6 +73,11 @@ def load() -> ctypes.CDLL:
                                                 vp, vp, vp, vp, i32, vp, i32,
                                                 i32, i32, i32, i32, i32, i32,
                                                 f32, i32, vp]
+        lib.pa_time_next_attention.argtypes = [vp, vp]
+        lib.pa_time_next_attention.restype = ctypes.c_int
+        lib.pa_decode_split.argtypes = [vp, vp, vp, i32, vp, vp, vp, vp, vp,
+                                        vp, i32, vp, i32, i32, i32, i32, i32,
+                                        i32, f32, i32, vp]
         lib.pa_decode_step_noalloc.argtypes = [vp, i32, vp, vp, vp, vp, vp,
                                                vp, i32, vp, i32, i32, i32,
                                                i32, i32, i32, f32, i32, vp]
@@ -88,6 +93,7 @@ def load() -> ctypes.CDLL:
         for fn in ("pa_cache_write", "pa_copy_blocks", "pa_decode",
                    "pa_decode_partitioned", "pa_decode_multi", "pa_decode_step",
                    "pa_decode_shared_prefix", "pa_decode_step_noalloc",
+                   "pa_decode_split",
                    "pa_reduce", "pa_read_ceiling"):
             getattr(lib, fn).restype = ctypes.c_int
         u64p = ctypes.POINTER(ctypes.c_uint64)
@@ -309,6 +315,59 @@ def pa_decode_step(max_logits, exp_sums, tmp_out, key_new, value_new, q,
     _check("pa_decode_step", lib.pa_decode_step(
         max_logits.data_ptr(), exp_sums.data_ptr(), tmp_out.data_ptr(),
         int(partition_size), pmax, key_new.data_ptr(), value_new.data_ptr(),
+        q.data_ptr(), k_pool.data_ptr(), v_pool.data_ptr(),
+        block_table.data_ptr(), mb, context_lens.data_ptr(), B, n_kv, G, d, bs,
+        n_blocks, float(scale), _dtype_code(q), _stream(stream)))
+
+
+def pa_time_next_attention(start_event, stop_event):
+    """Have the next attention kernel launched on this thread record its
+    own start/end in two torch.cuda.Event objects (created with
+    enable_timing=True); see include/pa.h.  None, None cancels."""
+    lib = load()
+
+    def handle(ev):
+        if ev is None:
+            return None
+        if not ev.cuda_event:       # torch creates its events lazily
+            ev.record()
+        return ev.cuda_event
+    _check("pa_time_next_attention",
+           lib.pa_time_next_attention(handle(start_event), handle(stop_event)))
+
+
+def pa_decode_split(max_logits, exp_sums, tmp_out, q, k_pool, v_pool,
+                    block_table, context_lens, *, scale, key_new=None,
+                    value_new=None, stream=None):
+    """The decode step with the context cut into pieces of equal runs of
+    tiles (workspace slots = pieces; max_partitions = the workspace's slot
+    count, at least 2); with key_new/value_new the new rows are written as
+    in pa_decode_step.  pa_reduce(..., partition_size=0) finishes."""
+    torch = _torch()
+    lib = load()
+    B, Hq, n_kv, G, d, bs, n_blocks, mb = _attention_common(
+        q, k_pool, v_pool, block_table, context_lens)
+    if (key_new is None) != (value_new is None):
+        raise ValueError("key_new and value_new go together")
+    if key_new is not None:
+        _dev("key_new", key_new, q.dtype, 3)
+        _dev("value_new", value_new, q.dtype, 3)
+        if tuple(key_new.shape) != (B, n_kv, d) or \
+                value_new.shape != key_new.shape:
+            raise ValueError("key_new/value_new must be [B, n_kv_heads, d_head]")
+    _dev("max_logits", max_logits, torch.float32, 3)
+    _dev("exp_sums", exp_sums, torch.float32, 3)
+    _dev("tmp_out", tmp_out, torch.float32, 4)
+    pmax = max_logits.shape[2]
+    if (tuple(max_logits.shape) != (B, Hq, pmax)
+            or tuple(exp_sums.shape) != (B, Hq, pmax)
+            or tuple(tmp_out.shape) != (B, Hq, pmax, d)):
+        raise ValueError("workspace shapes must be [B, Hq, PMAX] and "
+                         "[B, Hq, PMAX, D]")
+    _check("pa_decode_split", lib.pa_decode_split(
+        max_logits.data_ptr(), exp_sums.data_ptr(), tmp_out.data_ptr(), pmax,
+        None if key_new is None else key_new.data_ptr(),
+        None if value_new is None else value_new.data_ptr(),
         q.data_ptr(), k_pool.data_ptr(), v_pool.data_ptr(),
         block_table.data_ptr(), mb, context_lens.data_ptr(), B, n_kv, G, d, bs,
         n_blocks, float(scale), _dtype_code(q), _stream(stream)))

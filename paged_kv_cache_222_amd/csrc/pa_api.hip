@@ -139,10 +139,11 @@ hipError_t dispatch_attention(pa::AttnArgs a, int32_t dtype, int32_t d_head, int
   int64_t grid = rows * cols;
   a.persistent = 0;
   const int64_t slots = device_slots(dtype, d_head);
-  if (a.partition_size > 0 && a.batch <= pa::kPlanBatch && slots >= cols) {
-    // a whole number of work groups per column (KV head and head chunk)
+  if ((a.partition_size > 0 || a.split) && a.batch <= pa::kPlanBatch && slots >= cols) {
+    // a whole number of work groups per column (KV head and head chunk); a
+    // split launch fills the device whatever the batch
     a.persistent = 1;
-    grid = std::min(grid, slots - slots % cols);
+    grid = a.split ? slots - slots % cols : std::min(grid, slots - slots % cols);
   }
   // Shared-prefix items need the in-kernel plan and one query token; without
   // them every sequence reads its prefix through its own table (the same
@@ -256,9 +257,28 @@ void* scratch_address() {
   return p;
 }
 
+// Events set by pa_time_next_attention for the next attention launch of
+// this thread.
+thread_local hipEvent_t t_timing_start = nullptr;
+thread_local hipEvent_t t_timing_stop = nullptr;
+
 }  // namespace
 
+bool pa::take_attention_events(hipEvent_t* start, hipEvent_t* stop) {
+  if (!t_timing_start && !t_timing_stop) return false;
+  *start = t_timing_start;
+  *stop = t_timing_stop;
+  t_timing_start = t_timing_stop = nullptr;
+  return true;
+}
+
 extern "C" {
+
+int pa_time_next_attention(void* start_event, void* stop_event) {
+  t_timing_start = static_cast<hipEvent_t>(start_event);
+  t_timing_stop = static_cast<hipEvent_t>(stop_event);
+  return PA_OK;
+}
 
 const char* pa_strerror(int status) {
   switch (status) {
@@ -423,6 +443,43 @@ int pa_decode_shared_prefix(float* max_logits, float* exp_sums, float* tmp_out,
                             stream, key_new, value_new, prefix_len);
 }
 
+int pa_decode_split(float* max_logits, float* exp_sums, float* tmp_out, int32_t max_partitions,
+                    const void* key_new, const void* value_new, const void* q, void* k_pool,
+                    void* v_pool, const int32_t* block_table, int32_t max_blocks,
+                    const int32_t* context_lens, int32_t batch, int32_t n_kv_heads,
+                    int32_t gqa_group, int32_t d_head, int32_t block_size, int32_t n_blocks,
+                    float scale, int32_t dtype, void* stream) {
+  if (batch < 0) return PA_ERR_SHAPE;
+  if (batch == 0) return PA_OK;
+  if (!max_logits || !exp_sums || !tmp_out) return PA_ERR_NULL;
+  if ((key_new != nullptr) != (value_new != nullptr)) return PA_ERR_NULL;
+  if (key_new && (!aligned16(key_new) || !aligned16(value_new))) return PA_ERR_ALIGN;
+  const int st = check_attention(q, k_pool, v_pool, block_table, max_blocks, context_lens, batch,
+                                 n_kv_heads, gqa_group, d_head, block_size, n_blocks, dtype);
+  if (st != PA_OK) return st;
+  if (dtype == PA_F32) return PA_ERR_UNSUPPORTED;
+  if (max_partitions < 2) return PA_ERR_WORKSPACE;
+  // tile counts are summed in 32 bits
+  if ((int64_t)batch * (((int64_t)max_blocks * block_size + 15) / 16) > INT_MAX / 2 ||
+      (int64_t)batch * n_kv_heads * gqa_group > INT_MAX / 2)
+    return PA_ERR_SHAPE;
+  if (!aligned4(max_logits) || !aligned4(exp_sums) || !aligned16(tmp_out)) return PA_ERR_ALIGN;
+  pa::AttnArgs a = attention_args(q, k_pool, v_pool, block_table, max_blocks, context_lens,
+                                  batch, n_kv_heads, gqa_group, block_size, n_blocks, scale);
+  a.max_logits = max_logits;
+  a.exp_sums = exp_sums;
+  a.tmp_out = tmp_out;
+  a.partition_size = 0;
+  a.max_partitions = max_partitions;
+  a.split = 1;
+  a.key_new = key_new;
+  a.value_new = value_new;
+  (void)hipGetLastError();
+  int st2 = PA_OK;
+  const hipError_t e = dispatch_attention(a, dtype, d_head, batch, (hipStream_t)stream, &st2);
+  return st2 != PA_OK ? st2 : launch_status(e);
+}
+
 int pa_decode_multi(float* max_logits, float* exp_sums, float* tmp_out, int32_t partition_size,
                     int32_t max_partitions, const void* q, const void* k_pool,
                     const void* v_pool, const int32_t* block_table, int32_t max_blocks,
@@ -444,7 +501,7 @@ int pa_reduce(void* out, const float* max_logits, const float* exp_sums,
   if (!out || !max_logits || !exp_sums || !tmp_out || !context_lens) return PA_ERR_NULL;
   if (!dtype_ok(dtype) || !dhead_ok(d_head)) return PA_ERR_UNSUPPORTED;
   if (n_q_heads < 1) return PA_ERR_SHAPE;
-  if (partition_size <= 0) return PA_ERR_PARTITION;
+  if (partition_size < 0) return PA_ERR_PARTITION;   // 0: a split workspace
   if (max_partitions < 1) return PA_ERR_WORKSPACE;
   if ((int64_t)batch * n_q_heads > INT_MAX) return PA_ERR_SHAPE;
   if (!aligned16(out) || !aligned4(max_logits) || !aligned4(exp_sums) ||

@@ -332,7 +332,7 @@ __global__ __launch_bounds__(kAttnThreads) void attention_kernel(AttnArgs a) {
 template <Dt DT, int D, int GC>
 hipError_t launch_gc(const AttnArgs& a, unsigned grid, hipStream_t s) {
   constexpr int U = GC <= 4 ? 2 : 1;
-  hipLaunchKernelGGL((attention_kernel<DT, D, GC, U>), dim3(grid), dim3(kAttnThreads), 0, s, a);
+  launch_timed(attention_kernel<DT, D, GC, U>, dim3(grid), dim3(kAttnThreads), s, a);
   return hipGetLastError();
 }
 

@@ -246,7 +246,10 @@ __global__ __launch_bounds__(kAttnThreads, PA_MFMA_MIN_BLOCKS) void attention_mf
   // writes row (b * NQ + j) * Hq + kvh * G + g of q / out / the workspace,
   // and sees positions t < ctx - NQ + j + 1 (causal among the NQ tokens).
   const int K = a.n_kv_heads * a.n_hchunks;
-  const bool parts = a.partition_size > 0;
+  // Split launches (pa_decode_split): the workspace holds pieces of equal
+  // runs of tiles instead of fixed partitions (see the plan below).
+  const bool split = a.split != 0;
+  const bool parts = a.partition_size > 0 || split;
   const bool plan = parts && a.persistent;
   const int P = a.partition_size;
   const int64_t max_ctx = (int64_t)a.max_blocks << a.block_shift;
@@ -260,7 +263,62 @@ __global__ __launch_bounds__(kAttnThreads, PA_MFMA_MIN_BLOCKS) void attention_mf
   // read the same prefix tiles at about the same time; in the plan they
   // alternate with the full private partitions.
   int npp = 0, n_pre = 0, n_groups = 0;
-  if (plan) {
+  // Split plan: the tiles of a column are every sequence's 16-position
+  // tiles in sequence order (s_plan[b] = tiles before sequence b, s_plan[B]
+  // = all of them); work group jw of the column takes the run
+  // [jw * R, (jw + 1) * R) and writes one workspace slot per sequence the run
+  // touches: slot jw - s_plan[b] / R of sequence b.  R is the even share,
+  // raised where needed so that no sequence is cut into more than
+  // max_partitions pieces.  b_cur: the next sequence this work group visits.
+  int64_t sp_lo = 0, sp_hi = 0;
+  int sp_R = 1, b_cur = 0;
+  if (plan && split) {
+    const int B = a.batch;
+    int tl[4], ts = 0, tm = 0;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int b = threadIdx.x * 4 + j;
+      const int c = b < B ? a.context_lens[b] : 0;
+      // an invalid length gets one tile: its piece is written as NaN
+      tl[j] = b >= B ? 0 : (c >= 1 && (int64_t)c <= max_ctx) ? (c + 15) >> 4 : (c == 0 ? 0 : 1);
+      ts += tl[j];
+      tm = max(tm, tl[j]);
+    }
+    const int fi = wave_incl_scan(ts);
+#pragma unroll
+    for (int d = 1; d < kWave; d <<= 1) tm = max(tm, shfl_xor_i(tm, d));
+    if (lane == kWave - 1) {
+      s_m[wave][0] = __builtin_bit_cast(float, fi);
+      s_l[wave][0] = __builtin_bit_cast(float, tm);
+    }
+    __syncthreads();
+    int fo = 0, ftot = 0, tmax = 0;
+#pragma unroll
+    for (int w = 0; w < NW; ++w) {
+      const int fw = __builtin_bit_cast(int, s_m[w][0]);
+      if (w < wave) fo += fw;
+      ftot += fw;
+      tmax = max(tmax, __builtin_bit_cast(int, s_l[w][0]));
+    }
+    int fx = fo + fi - ts;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int b = threadIdx.x * 4 + j;
+      if (b < B) s_plan[b] = fx;
+      fx += tl[j];
+    }
+    if (threadIdx.x == 0) s_plan[B] = ftot;
+    __syncthreads();
+    const int Wc = (int)gridDim.x / K, jwc = (int)blockIdx.x / K;
+    const int PM = a.max_partitions;   // >= 2 (checked on the host)
+    sp_R = __builtin_amdgcn_readfirstlane(
+        max(max((ftot + Wc - 1) / Wc, (tmax + PM - 2) / (PM - 1)), 1));
+    sp_lo = (int64_t)jwc * sp_R;
+    sp_hi = min(sp_lo + sp_R, (int64_t)ftot);
+    b_cur = sp_lo < sp_hi ? plan_search(s_plan, B, (int)sp_lo) : B;
+    b_cur = __builtin_amdgcn_readfirstlane(b_cur);
+    n_items = 0;   // unused: the run decides
+  } else if (plan) {
     // Thread t owns sequences 4t..4t+3.  full(b) = partitions before b's
     // last one (and past the shared prefix), tail(b) = 1 if b has any; the
     // exclusive prefix sum of full(b), and the rank of b's final partition
@@ -395,10 +453,10 @@ __global__ __launch_bounds__(kAttnThreads, PA_MFMA_MIN_BLOCKS) void attention_mf
     __syncthreads();
     n_full = ftot;
     n_items = n_pre + ftot + ttot;  // per column
-  } else if (parts) {
+  } else if (parts && !split) {
     n_items = K * a.batch * a.max_partitions;
   } else {
-    n_items = K * a.batch;
+    n_items = K * a.batch;   // single pass, or a split launch without the plan
   }
 
   const float sl2 = a.scale_log2;
@@ -416,7 +474,22 @@ __global__ __launch_bounds__(kAttnThreads, PA_MFMA_MIN_BLOCKS) void attention_mf
   for (int it = 0;; ++it) {
     // ---- decode the item
     int kh, rr;
-    if (plan) {
+    // split launches: the piece's tile range [u0, u1) within the sequence,
+    // whether it is the sequence's last piece, and the sequence's piece count
+    int u0 = 0, u1 = 0, n_pieces = 1;
+    bool last_piece = true;
+    if (split && plan) {
+      kh = blockIdx.x % K;
+      rr = 0;
+      if (b_cur >= a.batch) break;
+      const int Sb = s_plan[b_cur];
+      if ((int64_t)Sb >= sp_hi) break;
+      const int Tb = s_plan[b_cur + 1] - Sb;
+      u0 = (int)max(sp_lo - Sb, (int64_t)0);
+      u1 = (int)min(sp_hi - Sb, (int64_t)Tb);
+      last_piece = (int64_t)Sb + Tb <= sp_hi;
+      n_pieces = (Sb + Tb - 1) / sp_R - Sb / sp_R + 1;
+    } else if (plan) {
       kh = blockIdx.x % K;
       rr = it * W + ((it & 1) ? W - 1 - jw : jw);
       if (rr >= n_items) break;
@@ -451,7 +524,17 @@ __global__ __launch_bounds__(kAttnThreads, PA_MFMA_MIN_BLOCKS) void attention_mf
         r2 = rr - n_pre;
       }
     }
-    if (pre) {
+    if (split && plan) {
+      b = b_cur;
+      p = jw - s_plan[b_cur] / sp_R;
+      // the next sequence with tiles
+      int nb = b_cur + 1;
+      while (nb < a.batch && s_plan[nb + 1] == s_plan[nb]) ++nb;
+      b_cur = __builtin_amdgcn_readfirstlane(nb);
+    } else if (split) {
+      b = rr;        // the whole sequence in one piece
+      u1 = INT32_MAX;
+    } else if (pre) {
       p = rp / n_groups;
       b = rp - p * n_groups;
     } else if (plan) {
@@ -494,6 +577,23 @@ __global__ __launch_bounds__(kAttnThreads, PA_MFMA_MIN_BLOCKS) void attention_mf
     int t0 = 0, t1 = ctx;
     if (pre) {
       t0 = p * P;
+    } else if (split) {
+      if (bad_ctx) {
+        // every slot of the row NaN (the piece's o too), so pa_reduce
+        // gives NaN whatever the slots held before
+        for (int idx = threadIdx.x; idx < gv * D; idx += kAttnThreads) {
+          const int g = idx / D, d = idx - g * D;
+          a.tmp_out[(row_of(g) * a.max_partitions + p) * D + d] = qnan;
+        }
+        for (int idx = threadIdx.x; idx < gv * a.max_partitions; idx += kAttnThreads) {
+          const int g = idx / a.max_partitions, q = idx - g * a.max_partitions;
+          a.max_logits[row_of(g) * a.max_partitions + q] = qnan;
+          a.exp_sums[row_of(g) * a.max_partitions + q] = qnan;
+        }
+        continue;
+      }
+      t0 = u0 * 16;
+      t1 = (int)min((int64_t)u1 * 16, (int64_t)ctx);
     } else if (parts) {
       const int64_t np = ctx > 0 ? ((int64_t)ctx + P - 1) / P : 0;
       if (np > a.max_partitions) {
@@ -883,6 +983,15 @@ __global__ __launch_bounds__(kAttnThreads, PA_MFMA_MIN_BLOCKS) void attention_mf
         if (d == 0) {
           a.max_logits[prow] = colbad[j] ? qnan : M * kLn2;
           a.exp_sums[prow] = colbad[j] ? qnan : L;
+          if (split && last_piece) {
+            // the sequence's unused slots: empty (exp_sums 0, pa_reduce
+            // skips them)
+            const int64_t r0 = row_of(g) * a.max_partitions;
+            for (int q = n_pieces; q < a.max_partitions; ++q) {
+              a.max_logits[r0 + q] = -__builtin_huge_valf();
+              a.exp_sums[r0 + q] = 0.0f;
+            }
+          }
         }
       } else {
         const int64_t o = row_of(g) * D + d;
@@ -897,9 +1006,9 @@ __global__ __launch_bounds__(kAttnThreads, PA_MFMA_MIN_BLOCKS) void attention_mf
 template <Dt DT>
 hipError_t launch_attention_mfma(const AttnArgs& a, int d_head, unsigned grid, hipStream_t s) {
   if (d_head == 64)
-    hipLaunchKernelGGL((attention_mfma_kernel<DT, 64>), dim3(grid), dim3(kAttnThreads), 0, s, a);
+    launch_timed(attention_mfma_kernel<DT, 64>, dim3(grid), dim3(kAttnThreads), s, a);
   else if (d_head == 128)
-    hipLaunchKernelGGL((attention_mfma_kernel<DT, 128>), dim3(grid), dim3(kAttnThreads), 0, s, a);
+    launch_timed(attention_mfma_kernel<DT, 128>, dim3(grid), dim3(kAttnThreads), s, a);
   else
     return hipErrorInvalidValue;
   return hipGetLastError();

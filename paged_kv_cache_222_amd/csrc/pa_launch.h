@@ -2,6 +2,7 @@
 // translation units.  Not part of the public header.
 #pragma once
 
+#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -49,9 +50,15 @@ struct AttnArgs {
   // write into a shared block, so it is a contract violation -- no write,
   // NaN outputs.  0: no such positions.
   int32_t shared_len;
+  // pa_decode_split: work groups take equal runs of the tiles of all
+  // sequences, writing one workspace slot per sequence piece
+  // (partition_size is 0).
+  int32_t split;
   float scale_log2;    // scale * log2(e)
 };
 
+// partition_size == 0: the workspace of pa_decode_split (every slot merged,
+// empty ones -- exp_sums 0 -- skipped).
 struct ReduceArgs {
   void* out;
   const float* max_logits;
@@ -120,6 +127,23 @@ struct ReadCeilingArgs {
   int64_t buf_tiles;          // tiles in the buffer (ids outside are skipped)
   int64_t tile_bytes;         // a multiple of 16
 };
+
+// Measurement aid behind pa_time_next_attention: if events were set on
+// this thread, hand them over (and clear them) so that the attention launch
+// records its own start and end in them.
+bool take_attention_events(hipEvent_t* start, hipEvent_t* stop);
+
+// A kernel launch that records its start and end in the events set by
+// pa_time_next_attention, if any (the timestamps of the dispatch itself),
+// and is an ordinary launch otherwise.
+template <typename F, typename... Args>
+void launch_timed(F kernel, dim3 grid, dim3 block, hipStream_t s, Args... args) {
+  hipEvent_t e0 = nullptr, e1 = nullptr;
+  if (take_attention_events(&e0, &e1))
+    hipExtLaunchKernelGGL(kernel, grid, block, 0, s, e0, e1, 0, args...);
+  else
+    hipLaunchKernelGGL(kernel, grid, block, 0, s, args...);
+}
 
 // Each returns a hipError_t from the launch.
 hipError_t launch_attention_f32(const AttnArgs& a, int d_head, int heads_per_chunk,

@@ -6,6 +6,13 @@
 // the mean of the o_p weighted by w_p = l_p exp(m_p - M), M = max_p m_p.
 // One wave per (sequence, query head), four per work group; lanes own
 // d_head/64 output elements.
+//
+// With partition_size == 0 the workspace holds the pieces of a split launch
+// (pa_decode_split): every slot is merged, and a slot with l = 0 (a piece
+// the sequence does not have) is skipped -- its o is never read into the
+// sum, so it need not be written.  Skipping l = 0 leaves the partitioned
+// results unchanged: there such a slot (a verify-pass token that sees
+// nothing) holds o = 0 and adds nothing.
 #include "pa_device.h"
 #include "pa_launch.h"
 
@@ -23,7 +30,7 @@ constexpr int kFewParts = 8;
 #endif
 constexpr int kRedRows = PA_REDUCE_ROWS;
 
-template <Dt DT, int D>
+template <Dt DT, int D, int FEW>
 __global__ __launch_bounds__(kWave * kRedRows) void reduce_few_kernel(ReduceArgs a) {
   constexpr int DPL = D / kWave;
   const int lane = threadIdx.x & (kWave - 1);
@@ -31,14 +38,14 @@ __global__ __launch_bounds__(kWave * kRedRows) void reduce_few_kernel(ReduceArgs
   if (bh64 >= (int64_t)a.batch * a.n_q_heads) return;
   const int bh = (int)bh64;
   const int b = bh / a.n_q_heads;
-  const int PM = a.max_partitions;  // <= kFewParts
+  const int PM = a.max_partitions;  // <= FEW
   const float* ml = a.max_logits + (int64_t)bh * PM;
   const float* es = a.exp_sums + (int64_t)bh * PM;
   const float* to = a.tmp_out + (int64_t)bh * PM * D + lane * DPL;
   const int ctx = a.context_lens[b];
-  float m[kFewParts], l[kFewParts], o[kFewParts][DPL];
+  float m[FEW], l[FEW], o[FEW][DPL];
 #pragma unroll
-  for (int p = 0; p < kFewParts; ++p) {
+  for (int p = 0; p < FEW; ++p) {
     if (p < PM) {
       m[p] = ml[p];
       l[p] = es[p];
@@ -48,7 +55,7 @@ __global__ __launch_bounds__(kWave * kRedRows) void reduce_few_kernel(ReduceArgs
   }
   const int64_t orow = (int64_t)bh * D;
   const int P = a.partition_size;
-  const int64_t np64 = ctx > 0 ? ((int64_t)ctx + P - 1) / P : 0;
+  const int64_t np64 = ctx > 0 ? (P > 0 ? ((int64_t)ctx + P - 1) / P : PM) : 0;
   if (ctx < 0 || np64 > PM || np64 == 0) {
     const float v = (np64 == 0 && ctx == 0) ? 0.0f : __builtin_nanf("");
 #pragma unroll
@@ -58,14 +65,14 @@ __global__ __launch_bounds__(kWave * kRedRows) void reduce_few_kernel(ReduceArgs
   const int np = (int)np64;
   float M = -__builtin_huge_valf();
 #pragma unroll
-  for (int p = 0; p < kFewParts; ++p)
+  for (int p = 0; p < FEW; ++p)
     if (p < np) M = fmaxf(M, m[p]);
   float W = 0.0f, acc[DPL];
 #pragma unroll
   for (int k = 0; k < DPL; ++k) acc[k] = 0.0f;
 #pragma unroll
-  for (int p = 0; p < kFewParts; ++p) {
-    if (p < np) {
+  for (int p = 0; p < FEW; ++p) {
+    if (p < np && l[p] != 0.0f) {
       const float w = l[p] * exp2_fast((m[p] - M) * kLog2e);
       W += w;
 #pragma unroll
@@ -90,7 +97,7 @@ __global__ __launch_bounds__(kWave * kRedRows) void reduce_kernel(ReduceArgs a) 
   const int ctx = a.context_lens[b];
   const int P = a.partition_size;
   const int64_t orow = (int64_t)bh * D;
-  const int64_t np64 = ctx > 0 ? ((int64_t)ctx + P - 1) / P : 0;
+  const int64_t np64 = ctx > 0 ? (P > 0 ? ((int64_t)ctx + P - 1) / P : a.max_partitions) : 0;
   if (ctx < 0 || np64 > a.max_partitions || np64 == 0) {
     const float v = (np64 == 0 && ctx == 0) ? 0.0f : __builtin_nanf("");
 #pragma unroll
@@ -130,13 +137,16 @@ __global__ __launch_bounds__(kWave * kRedRows) void reduce_kernel(ReduceArgs a) 
 #pragma unroll
         for (int k = 0; k < DPL; ++k) oj[u][k] = to[(int64_t)(p0 + j + u) * D + k];
       }
+      // a zero weight (an empty slot) is skipped: its o may be unwritten
 #pragma unroll
       for (int u = 0; u < 4; ++u)
 #pragma unroll
-        for (int k = 0; k < DPL; ++k) acc[k] = __builtin_fmaf(wj[u], oj[u][k], acc[k]);
+        for (int k = 0; k < DPL; ++k)
+          acc[k] = wj[u] != 0.0f ? __builtin_fmaf(wj[u], oj[u][k], acc[k]) : acc[k];
     }
     for (; j < n; ++j) {
       const float wj = as_f(__builtin_amdgcn_readlane((int)as_u(w), j));
+      if (wj == 0.0f) continue;
 #pragma unroll
       for (int k = 0; k < DPL; ++k)
         acc[k] = __builtin_fmaf(wj, to[(int64_t)(p0 + j) * D + k], acc[k]);
@@ -153,16 +163,24 @@ template <Dt DT>
 static hipError_t launch_reduce_dt(const ReduceArgs& a, int d_head, hipStream_t s) {
   const unsigned grid = (unsigned)(((int64_t)a.batch * a.n_q_heads + kRedRows - 1) / kRedRows);
   const bool few = a.max_partitions <= kFewParts;
+  // split workspaces of up to 16 pieces also take one round trip (for
+  // partitioned workspaces of 9-16 the general loop measured faster)
+  const bool few16 = !few && a.partition_size == 0 && a.max_partitions <= 2 * kFewParts;
+  const dim3 g(grid), t(kWave * kRedRows);
   if (d_head == 64) {
     if (few)
-      hipLaunchKernelGGL((reduce_few_kernel<DT, 64>), dim3(grid), dim3(kWave * kRedRows), 0, s, a);
+      hipLaunchKernelGGL((reduce_few_kernel<DT, 64, kFewParts>), g, t, 0, s, a);
+    else if (few16)
+      hipLaunchKernelGGL((reduce_few_kernel<DT, 64, 2 * kFewParts>), g, t, 0, s, a);
     else
-      hipLaunchKernelGGL((reduce_kernel<DT, 64>), dim3(grid), dim3(kWave * kRedRows), 0, s, a);
+      hipLaunchKernelGGL((reduce_kernel<DT, 64>), g, t, 0, s, a);
   } else if (d_head == 128) {
     if (few)
-      hipLaunchKernelGGL((reduce_few_kernel<DT, 128>), dim3(grid), dim3(kWave * kRedRows), 0, s, a);
+      hipLaunchKernelGGL((reduce_few_kernel<DT, 128, kFewParts>), g, t, 0, s, a);
+    else if (few16)
+      hipLaunchKernelGGL((reduce_few_kernel<DT, 128, 2 * kFewParts>), g, t, 0, s, a);
     else
-      hipLaunchKernelGGL((reduce_kernel<DT, 128>), dim3(grid), dim3(kWave * kRedRows), 0, s, a);
+      hipLaunchKernelGGL((reduce_kernel<DT, 128>), g, t, 0, s, a);
   } else {
     return hipErrorInvalidValue;
   }

@@ -31,12 +31,12 @@ def test_header_declares_the_entry_points():
     assert declared_functions() == sorted(
         ["pa_block_hashes", "pa_cache_write", "pa_copy_blocks", "pa_decode",
          "pa_decode_multi", "pa_decode_partitioned",
-         "pa_decode_shared_prefix", "pa_decode_step",
+         "pa_decode_shared_prefix", "pa_decode_split", "pa_decode_step",
          "pa_decode_step_noalloc", "pa_pool_alloc",
          "pa_pool_available", "pa_pool_create", "pa_pool_destroy",
          "pa_pool_fork", "pa_pool_map_prefix", "pa_pool_refcount",
          "pa_pool_release", "pa_pool_simulate", "pa_read_ceiling",
-         "pa_reduce", "pa_strerror"])
+         "pa_reduce", "pa_strerror", "pa_time_next_attention"])
 
 
 def test_library_exports_every_declared_symbol(lib):
@@ -234,6 +234,35 @@ def test_noalloc_argument_checks(lib):
         PA_ERR_SCRATCH
 
 
+def _split(lib, **kw):
+    a = dict(ml=P, es=P, to=P, pmax=8, kn=P, vn=P, q=P, k=P, v=P, tbl=P,
+             mb=64, ctx=P, B=4, hkv=2, G=4, d=128, bs=16, nb=32, scale=0.1,
+             dt=2)
+    a.update(kw)
+    return lib.pa_decode_split(
+        a["ml"], a["es"], a["to"], a["pmax"], a["kn"], a["vn"], a["q"],
+        a["k"], a["v"], a["tbl"], a["mb"], a["ctx"], a["B"], a["hkv"],
+        a["G"], a["d"], a["bs"], a["nb"], a["scale"], a["dt"], None)
+
+
+def test_split_argument_checks(lib):
+    assert _split(lib, B=0) == PA_OK
+    for k in ("ml", "es", "to", "q", "k", "v", "tbl", "ctx"):
+        assert _split(lib, **{k: None}) == PA_ERR_NULL, k
+    assert _split(lib, kn=None) == PA_ERR_NULL        # only as a pair
+    assert _split(lib, kn=MIS) == PA_ERR_ALIGN
+    assert _split(lib, to=MIS) == PA_ERR_ALIGN
+    assert _split(lib, pmax=1) == PA_ERR_WORKSPACE    # at least two slots
+    assert _split(lib, dt=0, d=64) == PA_ERR_UNSUPPORTED   # fp32
+    assert _split(lib, d=32) == PA_ERR_UNSUPPORTED
+    # tile counts must fit 32 bits
+    assert _split(lib, B=1024, mb=1 << 20) == PA_ERR_SHAPE
+
+
+def test_timing_hook_accepts_and_cancels(lib):
+    assert lib.pa_time_next_attention(None, None) == PA_OK
+
+
 def _prefix(lib, **kw):
     a = dict(ml=P, es=P, to=P, psz=512, pmax=4, kn=P, vn=P, q=P, k=P, v=P,
              tbl=P, mb=64, ctx=P, B=4, hkv=2, G=4, d=128, bs=16, nb=32,
@@ -295,7 +324,7 @@ def test_reduce_argument_checks(lib):
     assert _red(lib, d=100) == PA_ERR_UNSUPPORTED
     assert _red(lib, dt=9) == PA_ERR_UNSUPPORTED
     assert _red(lib, hq=0) == PA_ERR_SHAPE
-    assert _red(lib, psz=0) == PA_ERR_PARTITION
+    assert _red(lib, psz=-1) == PA_ERR_PARTITION   # 0: a split workspace
     assert _red(lib, pmax=0) == PA_ERR_WORKSPACE
     assert _red(lib, out=MIS) == PA_ERR_ALIGN
 
