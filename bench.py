@@ -110,7 +110,7 @@ def algorithmic_bytes(w):
 # The form each batch's line reports by default (--variant all): the fastest
 # form measured on MI355X for that batch (a batch with a shared prefix
 # reports "prefix").
-HEADLINE_FORM = {"llama3-8b": "fused", "qwen2.5-1.5b": "split",
+HEADLINE_FORM = {"llama3-8b": "fused", "qwen2.5-1.5b": "fused",
                  "llama2-7b": "fused", "tiny": "fused"}
 
 # sources whose change invalidates the HBM byte counts stored under profiles/
