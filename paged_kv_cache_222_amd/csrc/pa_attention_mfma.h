@@ -966,17 +966,20 @@ __global__ __launch_bounds__(kAttnThreads, PA_MFMA_MIN_BLOCKS) void attention_mf
       for (int k = 0; k < 4; ++k) r[k] = colbad[j] ? qnan : (L > 0.0f ? Ov[k] / L : 0.0f);
       if (parts) {
         const int64_t prow = row_of(g) * a.max_partitions + p;
-        // With shared items the prefix tiles live in L2: the partial
-        // outputs go non-temporal rather than evict them (shared-prefix
-        // batch, all stores non-temporal: 593 -> 575 us at P 2048, 670 ->
-        // 636 us at P 512; without shared items ordinary stores are faster
-        // by ~1 %).
+        // With shared items the prefix tiles live in L2, and the partial
+        // outputs are written at system scope (sc0 sc1): they pass L2 by
+        // instead of evicting the prefix, and the reduce that follows finds
+        // them in the memory-side cache.  Shared-prefix batch, P 512:
+        // non-temporal stores 621 us, sc0 sc1 617 us (and its reduce 15.6
+        // -> 13.2 us), where ordinary stores had cost ~5 % more than
+        // non-temporal ones; P 2048 unchanged at 556 us.  Without
+        // shared items ordinary stores are the fastest (LLaMA-3 batch 146
+        // us against 148 us with sc0 sc1).  A vector store; gfx9 counts it
+        // in vmcnt, and vector memory operations complete in issue order,
+        // so the waits the compiler places for its own loads stay correct.
         if (n_pre > 0) {
-          // the empty asm on both sides keeps the compiler from merging the
-          // two stores (and dropping the hint)
-          asm volatile("" ::: "memory");
-          __builtin_nontemporal_store(r, reinterpret_cast<f32x4_t*>(&a.tmp_out[prow * D + d]));
-          asm volatile("" ::: "memory");
+          float* sp = &a.tmp_out[prow * D + d];
+          asm volatile("global_store_dwordx4 %0, %1, off sc0 sc1" : : "v"(sp), "v"(r) : "memory");
         } else {
           *reinterpret_cast<f32x4_t*>(&a.tmp_out[prow * D + d]) = r;
         }
