@@ -11,7 +11,10 @@ line reports the batch's headline form (see HEADLINE_FORM), the others'
 times beside it (--variant best reports the fastest instead).  A batch
 whose rows share a prompt's blocks also times "prefix"
 (pa_decode_shared_prefix with the write folded in, then pa_reduce) and
-reports that.  Inputs are seeded synthetic batches (see
+reports that.  "vector" (pa_cache_write, pa_decode_partitioned_vector,
+pa_reduce: the partitioned form on the vector-ALU kernel) is timed only
+when asked for, to set the two engines side by side.  Inputs are seeded
+synthetic batches (see
 paged_kv_cache_222_amd/workloads.py); the default is the LLaMA-3-8B-shaped
 GQA batch (B=128, 32/8 heads, d128, bf16, log-normal context lengths).
 Several copies of the inputs are resident in HBM and the steps rotate over
@@ -57,14 +60,20 @@ def parse():
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--block-size", type=int, default=None)
     ap.add_argument("--partition-size", type=int, default=None)
-    ap.add_argument("--copies", type=int, default=3,
-                    help="resident input copies the steps rotate over")
+    ap.add_argument("--copies", type=int, default=None,
+                    help="resident input copies the steps rotate over "
+                         "(default: enough that 1 GiB of other K/V reads "
+                         "comes between two uses of a copy, at least 3)")
     ap.add_argument("--variant", choices=["all", "best", "fused", "split",
-                                          "partitioned", "single", "prefix"],
+                                          "partitioned", "single", "prefix",
+                                          "vector"],
                     default="all",
                     help="all (default): time every form, report the fused "
                          "step (the shared-prefix step for a batch with a "
-                         "shared prefix); best: report the fastest form")
+                         "shared prefix); best: report the fastest form; "
+                         "vector: the partitioned form on the vector-ALU "
+                         "kernel (pa_decode_partitioned_vector), timed only "
+                         "when asked for")
     ap.add_argument("--slots", type=int, default=None,
                     help="split form: workspace slots per row (default: the "
                          "fewest that let every work group take an even "
@@ -115,6 +124,7 @@ HEADLINE_FORM = {"llama3-8b": "fused", "qwen2.5-1.5b": "fused",
 
 # sources whose change invalidates the HBM byte counts stored under profiles/
 KERNEL_SOURCES = ["pa_attention_mfma.h", "pa_attention_mfma.hip",
+                  "pa_attention.h", "pa_attention_vector.hip",
                   "pa_launch.h", "pa_device.h", "pa_api.hip"]
 
 
@@ -133,11 +143,12 @@ def measured_traffic(name, variant, P, block_size):
     profiles/ (FETCH_SIZE + WRITE_SIZE, each scaled by the copy-kernel
     factor), or None when there is none for this workload or the kernel
     sources changed since it was taken."""
+    kernel = "attention_vector" if variant == "vector" else "attention_mfma"
     path = os.path.join(ROOT, "profiles",
-                        f"attention_mfma_{name}_P{P}_hbm_counters.txt")
+                        f"{kernel}_{name}_P{P}_hbm_counters.txt")
     if not os.path.exists(path):
         path = os.path.join(ROOT, "profiles",
-                            f"attention_mfma_{name}_hbm_counters.txt")
+                            f"{kernel}_{name}_hbm_counters.txt")
     if not os.path.exists(path):
         return None
     kv = {}
@@ -155,6 +166,17 @@ def measured_traffic(name, variant, P, block_size):
         return int(kv["traffic_bytes_per_launch"])
     except (KeyError, ValueError):
         return None
+
+
+def n_copies(args, w):
+    """Resident input copies the steps rotate over: --copies, else enough
+    that at least 1 GiB of other K/V reads (four times the 256 MB last-level
+    cache) falls between two steps on the same copy; 3 to 16 (a batch too
+    small for 16 copies to leave the cache is cache-resident anyway)."""
+    if args.copies:
+        return args.copies
+    per_step = w.kv_bytes_unique() if w.cfg.prefix_len else w.kv_bytes_logical()
+    return min(16, max(3, 1 + -(-(1 << 30) // max(1, per_step))))
 
 
 def split_slots(w, torch):
@@ -330,7 +352,7 @@ def bench_verify(args, torch, pa, wl):
         (c.batch * k, c.n_kv_heads, c.d_head), dtype=np.float32), c.dtype)
     copies = [dict(k=up(w.k_pool, tdt), v=up(w.v_pool, tdt), q=up(qm, tdt),
                    kn=up(kv_new, tdt), vn=up(kv_new, tdt))
-              for _ in range(args.copies)]
+              for _ in range(n_copies(args, w))]
     tbl, cl = up(w.block_table), up(w.context_lens)
     B, Hq, D = c.batch, c.n_q_heads, c.d_head
     ws = pa.partition_workspace(B, k * Hq, D, pmax)
@@ -400,7 +422,9 @@ def bench_verify(args, torch, pa, wl):
                      "achieved": round(alg / (attn_us * 1e-6) / 1e9, 1),
                      "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(alg / (attn_us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
-                     "traffic": None, "algorithmic_bytes_per_launch": alg,
+                     "traffic": measured_traffic(f"{c.name}_verify{k}",
+                                                 "multi", P, c.block_size),
+                     "algorithmic_bytes_per_launch": alg,
                      "avg_launch_us": round(attn_us, 3)},
     }
     if not args.no_cpu_baseline:
@@ -609,7 +633,7 @@ def main():
         return torch.from_numpy(np.ascontiguousarray(x)).cuda()
 
     copies = []
-    for i in range(args.copies):
+    for i in range(n_copies(args, w)):
         copies.append(dict(k=up(w.k_pool, tdt), v=up(w.v_pool, tdt),
                            q=up(w.q, tdt), kn=up(w.key_new, tdt),
                            vn=up(w.value_new, tdt)))
@@ -666,8 +690,10 @@ def main():
             if ev is not None:
                 ev[2].record(stream)
         else:
+            # "vector": the same launch on the vector-ALU kernel
             pa.pa_decode_partitioned(*ws, x["q"], x["k"], x["v"], tbl, cl,
-                                     partition_size=P, scale=w.scale)
+                                     partition_size=P, scale=w.scale,
+                                     vector=variant == "vector")
             if ev is not None:
                 ev[2].record(stream)
             pa.pa_reduce(out, *ws, cl, partition_size=P)
@@ -734,7 +760,9 @@ def main():
               "split": "attention_mfma_kernel (pa_decode_split)",
               "prefix": "attention_mfma_kernel (pa_decode_shared_prefix)",
               "partitioned": "attention_mfma_kernel (pa_decode_partitioned)",
-              "single": "attention_mfma_kernel (pa_decode)"}[best]
+              "single": "attention_mfma_kernel (pa_decode)",
+              "vector": "attention_kernel, vector ALU "
+                        "(pa_decode_partitioned_vector)"}[best]
     rec = {
         "metric": METRIC,
         "value": round(gbs, 2),

@@ -209,6 +209,28 @@ int pa_decode_partitioned(float* max_logits, float* exp_sums, float* tmp_out,
                           float scale, int32_t dtype, void* stream);
 
 /*
+ * pa_decode_partitioned_vector -- pa_decode_partitioned computed by the
+ * vector-ALU kernel (the one fp32 caches use) for every dtype, where
+ * pa_decode_partitioned runs fp16 and bf16 on the matrix cores.  A
+ * measurement aid: decode reads each cached byte once and spends only a
+ * multiply-add or two on it ("Serving", section 23.2), and this entry
+ * point times the two engines on the same batch.  Arguments, outputs,
+ * layout, errors and NaN rules are those of pa_decode_partitioned; the
+ * values agree with it to rounding (the sums run in another order).
+ */
+int pa_decode_partitioned_vector(float* max_logits, float* exp_sums,
+                                 float* tmp_out, int32_t partition_size,
+                                 int32_t max_partitions, const void* q,
+                                 const void* k_pool, const void* v_pool,
+                                 const int32_t* block_table,
+                                 int32_t max_blocks,
+                                 const int32_t* context_lens, int32_t batch,
+                                 int32_t n_kv_heads, int32_t gqa_group,
+                                 int32_t d_head, int32_t block_size,
+                                 int32_t n_blocks, float scale, int32_t dtype,
+                                 void* stream);
+
+/*
  * pa_decode_step -- a whole decode step for the partitioned path: the cache
  * write of each sequence's new token folded into pa_decode_partitioned.
  * For every sequence with n = context_lens[b] >= 1 whose table entry for

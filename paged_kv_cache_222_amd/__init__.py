@@ -19,6 +19,7 @@ from ._binding import (  # noqa: F401
     pa_decode,
     pa_decode_multi,
     pa_decode_partitioned,
+    pa_decode_partitioned_vector,
     pa_decode_shared_prefix,
     pa_decode_split,
     pa_decode_step,

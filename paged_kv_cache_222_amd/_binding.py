@@ -85,13 +85,15 @@ def load() -> ctypes.CDLL:
                                         i32, vp, vp]
         lib.pa_decode.argtypes = [vp, vp, vp, vp, vp, i32, vp, i32, i32, i32,
                                   i32, i32, i32, f32, i32, vp]
-        lib.pa_decode_partitioned.argtypes = [vp, vp, vp, i32, i32, vp, vp, vp,
-                                              vp, i32, vp, i32, i32, i32, i32,
-                                              i32, i32, f32, i32, vp]
+        for fn in ("pa_decode_partitioned", "pa_decode_partitioned_vector"):
+            getattr(lib, fn).argtypes = [vp, vp, vp, i32, i32, vp, vp, vp, vp,
+                                         i32, vp, i32, i32, i32, i32, i32, i32,
+                                         f32, i32, vp]
         lib.pa_reduce.argtypes = [vp, vp, vp, vp, vp, i32, i32, i32, i32, i32,
                                   i32, vp]
         for fn in ("pa_cache_write", "pa_copy_blocks", "pa_decode",
-                   "pa_decode_partitioned", "pa_decode_multi", "pa_decode_step",
+                   "pa_decode_partitioned", "pa_decode_partitioned_vector",
+                   "pa_decode_multi", "pa_decode_step",
                    "pa_decode_shared_prefix", "pa_decode_step_noalloc",
                    "pa_decode_split",
                    "pa_reduce", "pa_read_ceiling"):
@@ -265,9 +267,11 @@ def pa_decode(out, q, k_pool, v_pool, block_table, context_lens, *, scale,
 
 def pa_decode_partitioned(max_logits, exp_sums, tmp_out, q, k_pool, v_pool,
                           block_table, context_lens, *, partition_size, scale,
-                          stream=None):
+                          stream=None, vector=False):
     """Per-partition softmax statistics into the fp32 workspace
-    (max_logits/exp_sums [B, Hq, PMAX], tmp_out [B, Hq, PMAX, D])."""
+    (max_logits/exp_sums [B, Hq, PMAX], tmp_out [B, Hq, PMAX, D]).
+    ``vector=True`` calls pa_decode_partitioned_vector: the same results
+    from the vector-ALU kernel, for timing it beside the matrix-core one."""
     torch = _torch()
     lib = load()
     B, Hq, n_kv, G, d, bs, n_blocks, mb = _attention_common(
@@ -281,12 +285,23 @@ def pa_decode_partitioned(max_logits, exp_sums, tmp_out, q, k_pool, v_pool,
             or tuple(tmp_out.shape) != (B, Hq, pmax, d)):
         raise ValueError("workspace shapes must be [B, Hq, PMAX] and "
                          "[B, Hq, PMAX, D]")
-    _check("pa_decode_partitioned", lib.pa_decode_partitioned(
+    fn = "pa_decode_partitioned_vector" if vector else "pa_decode_partitioned"
+    _check(fn, getattr(lib, fn)(
         max_logits.data_ptr(), exp_sums.data_ptr(), tmp_out.data_ptr(),
         int(partition_size), pmax, q.data_ptr(), k_pool.data_ptr(),
         v_pool.data_ptr(), block_table.data_ptr(), mb, context_lens.data_ptr(),
         B, n_kv, G, d, bs, n_blocks, float(scale), _dtype_code(q),
         _stream(stream)))
+
+
+def pa_decode_partitioned_vector(max_logits, exp_sums, tmp_out, q, k_pool,
+                                 v_pool, block_table, context_lens, *,
+                                 partition_size, scale, stream=None):
+    """pa_decode_partitioned on the vector-ALU kernel for every dtype."""
+    pa_decode_partitioned(max_logits, exp_sums, tmp_out, q, k_pool, v_pool,
+                          block_table, context_lens,
+                          partition_size=partition_size, scale=scale,
+                          stream=stream, vector=True)
 
 
 def pa_decode_step(max_logits, exp_sums, tmp_out, key_new, value_new, q,

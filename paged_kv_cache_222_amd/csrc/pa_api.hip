@@ -170,7 +170,8 @@ int decode_partitioned(float* max_logits, float* exp_sums, float* tmp_out,
                        int32_t n_queries, int32_t n_kv_heads, int32_t gqa_group,
                        int32_t d_head, int32_t block_size, int32_t n_blocks, float scale,
                        int32_t dtype, void* stream, const void* key_new = nullptr,
-                       const void* value_new = nullptr, int32_t prefix_len = 0) {
+                       const void* value_new = nullptr, int32_t prefix_len = 0,
+                       bool vector = false) {
   if (batch < 0 || n_queries < 1) return PA_ERR_SHAPE;
   if (batch == 0) return PA_OK;
   if (!max_logits || !exp_sums || !tmp_out) return PA_ERR_NULL;
@@ -225,6 +226,19 @@ int decode_partitioned(float* max_logits, float* exp_sums, float* tmp_out,
       a.key_new = key_new;
       a.value_new = value_new;
     }
+  }
+  if (vector) {
+    // the vector-ALU kernel for any dtype (one query token, no folded write)
+    const unsigned grid = (unsigned)(rows * n_kv_heads * a.n_hchunks);
+    const hipError_t e =
+        dtype == PA_F32
+            ? pa::launch_attention_f32(a, d_head, a.heads_per_chunk, grid, (hipStream_t)stream)
+        : dtype == PA_F16
+            ? pa::launch_attention_vector_f16(a, d_head, a.heads_per_chunk, grid,
+                                              (hipStream_t)stream)
+            : pa::launch_attention_vector_bf16(a, d_head, a.heads_per_chunk, grid,
+                                               (hipStream_t)stream);
+    return launch_status(e);
   }
   int st2 = PA_OK;
   const hipError_t e = dispatch_attention(a, dtype, d_head, rows, (hipStream_t)stream, &st2);
@@ -414,6 +428,20 @@ int pa_decode_partitioned(float* max_logits, float* exp_sums, float* tmp_out,
                             k_pool, v_pool, block_table, max_blocks, context_lens, batch, 1,
                             n_kv_heads, gqa_group, d_head, block_size, n_blocks, scale, dtype,
                             stream);
+}
+
+int pa_decode_partitioned_vector(float* max_logits, float* exp_sums, float* tmp_out,
+                                 int32_t partition_size, int32_t max_partitions, const void* q,
+                                 const void* k_pool, const void* v_pool,
+                                 const int32_t* block_table, int32_t max_blocks,
+                                 const int32_t* context_lens, int32_t batch,
+                                 int32_t n_kv_heads, int32_t gqa_group, int32_t d_head,
+                                 int32_t block_size, int32_t n_blocks, float scale,
+                                 int32_t dtype, void* stream) {
+  return decode_partitioned(max_logits, exp_sums, tmp_out, partition_size, max_partitions, q,
+                            k_pool, v_pool, block_table, max_blocks, context_lens, batch, 1,
+                            n_kv_heads, gqa_group, d_head, block_size, n_blocks, scale, dtype,
+                            stream, nullptr, nullptr, 0, true);
 }
 
 int pa_decode_step(float* max_logits, float* exp_sums, float* tmp_out, int32_t partition_size,

@@ -148,6 +148,10 @@ void launch_timed(F kernel, dim3 grid, dim3 block, hipStream_t s, Args... args) 
 // Each returns a hipError_t from the launch.
 hipError_t launch_attention_f32(const AttnArgs& a, int d_head, int heads_per_chunk,
                                 unsigned grid, hipStream_t s);
+hipError_t launch_attention_vector_f16(const AttnArgs& a, int d_head, int heads_per_chunk,
+                                       unsigned grid, hipStream_t s);
+hipError_t launch_attention_vector_bf16(const AttnArgs& a, int d_head, int heads_per_chunk,
+                                        unsigned grid, hipStream_t s);
 hipError_t launch_attention_mfma_f16(const AttnArgs& a, int d_head, unsigned grid,
                                      hipStream_t s);
 hipError_t launch_attention_mfma_bf16(const AttnArgs& a, int d_head, unsigned grid,

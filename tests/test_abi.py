@@ -31,7 +31,7 @@ def test_header_declares_the_entry_points():
     assert declared_functions() == sorted(
         ["pa_block_hashes", "pa_cache_write", "pa_copy_blocks", "pa_decode",
          "pa_decode_multi", "pa_decode_partitioned",
-         "pa_decode_shared_prefix", "pa_decode_split", "pa_decode_step",
+         "pa_decode_partitioned_vector", "pa_decode_shared_prefix", "pa_decode_split", "pa_decode_step",
          "pa_decode_step_noalloc", "pa_pool_alloc",
          "pa_pool_available", "pa_pool_create", "pa_pool_destroy",
          "pa_pool_fork", "pa_pool_map_prefix", "pa_pool_refcount",
@@ -137,27 +137,31 @@ def test_decode_argument_checks(lib):
     assert _dec(lib, tbl=P + 2) == PA_ERR_ALIGN
 
 
-def _part(lib, **kw):
+def _part(lib, fn="pa_decode_partitioned", **kw):
     a = dict(ml=P, es=P, to=P, psz=512, pmax=4, q=P, k=P, v=P, tbl=P, mb=64,
              ctx=P, B=4, hkv=2, G=4, d=128, bs=16, nb=32, scale=0.1, dt=2)
     a.update(kw)
-    return lib.pa_decode_partitioned(
+    return getattr(lib, fn)(
         a["ml"], a["es"], a["to"], a["psz"], a["pmax"], a["q"], a["k"],
         a["v"], a["tbl"], a["mb"], a["ctx"], a["B"], a["hkv"], a["G"], a["d"],
         a["bs"], a["nb"], a["scale"], a["dt"], None)
 
 
-def test_partitioned_argument_checks(lib):
-    assert _part(lib, B=0) == PA_OK
+@pytest.mark.parametrize("fn", ["pa_decode_partitioned",
+                                "pa_decode_partitioned_vector"])
+def test_partitioned_argument_checks(lib, fn):
+    def call(**kw):
+        return _part(lib, fn, **kw)
+    assert call(B=0) == PA_OK
     for k in ("ml", "es", "to", "q", "tbl"):
-        assert _part(lib, **{k: None}) == PA_ERR_NULL, k
-    assert _part(lib, psz=0) == PA_ERR_PARTITION
-    assert _part(lib, psz=24) == PA_ERR_PARTITION     # not a multiple of 16
-    assert _part(lib, psz=-16) == PA_ERR_PARTITION
-    assert _part(lib, pmax=0) == PA_ERR_WORKSPACE
-    assert _part(lib, d=256) == PA_ERR_UNSUPPORTED
-    assert _part(lib, to=MIS) == PA_ERR_ALIGN
-    assert _part(lib, pmax=2**20, B=2**12) == PA_ERR_SHAPE   # grid too large
+        assert call(**{k: None}) == PA_ERR_NULL, k
+    assert call(psz=0) == PA_ERR_PARTITION
+    assert call(psz=24) == PA_ERR_PARTITION     # not a multiple of 16
+    assert call(psz=-16) == PA_ERR_PARTITION
+    assert call(pmax=0) == PA_ERR_WORKSPACE
+    assert call(d=256) == PA_ERR_UNSUPPORTED
+    assert call(to=MIS) == PA_ERR_ALIGN
+    assert call(pmax=2**20, B=2**12) == PA_ERR_SHAPE   # grid too large
 
 
 def _multi(lib, **kw):
