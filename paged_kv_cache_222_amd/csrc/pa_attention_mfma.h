@@ -199,7 +199,16 @@ __device__ __forceinline__ int plan_search(const int* pre, int n, int r) {
   return lo;
 }
 
-template <Dt DT, int D>
+// Launch modes, each its own instantiation so that a launch carries no code
+// of the others (the split and shared-prefix paths in the plain kernel cost
+// 52 more spilled scalar registers and ~2 us on a 35 us launch).
+enum AttnMode : int {
+  kModePlain = 0,   // single pass, or partitions (with or without the plan)
+  kModePrefix = 1,  // partitions with shared-prefix items
+  kModeSplit = 2,   // pa_decode_split: pieces of equal runs of tiles
+};
+
+template <Dt DT, int D, int MODE>
 #ifndef PA_MFMA_MIN_BLOCKS
 #define PA_MFMA_MIN_BLOCKS 2  // work groups per CU the register budget must allow
 #endif
@@ -248,7 +257,7 @@ __global__ __launch_bounds__(kAttnThreads, PA_MFMA_MIN_BLOCKS) void attention_mf
   const int K = a.n_kv_heads * a.n_hchunks;
   // Split launches (pa_decode_split): the workspace holds pieces of equal
   // runs of tiles instead of fixed partitions (see the plan below).
-  const bool split = a.split != 0;
+  constexpr bool split = MODE == kModeSplit;
   const bool parts = a.partition_size > 0 || split;
   const bool plan = parts && a.persistent;
   const int P = a.partition_size;
@@ -331,7 +340,7 @@ __global__ __launch_bounds__(kAttnThreads, PA_MFMA_MIN_BLOCKS) void attention_mf
       const int b = threadIdx.x * 4 + j;
       cs[j] = b < B ? a.context_lens[b] : 0;
     }
-    if (a.prefix_parts > 0) {
+    if (MODE == kModePrefix && a.prefix_parts > 0) {
       if (threadIdx.x < kPlanBatch / 32) s_inval[threadIdx.x] = 0u;
       // Only partitions before every valid sequence's final one are shared
       // items, so each sequence's final partition (the one holding the new
@@ -1006,27 +1015,45 @@ __global__ __launch_bounds__(kAttnThreads, PA_MFMA_MIN_BLOCKS) void attention_mf
   }
 }
 
-template <Dt DT>
-hipError_t launch_attention_mfma(const AttnArgs& a, int d_head, unsigned grid, hipStream_t s) {
-  if (d_head == 64)
-    launch_timed(attention_mfma_kernel<DT, 64>, dim3(grid), dim3(kAttnThreads), s, a);
-  else if (d_head == 128)
-    launch_timed(attention_mfma_kernel<DT, 128>, dim3(grid), dim3(kAttnThreads), s, a);
+template <Dt DT, int D>
+hipError_t launch_attention_mfma_d(const AttnArgs& a, unsigned grid, hipStream_t s) {
+  if (a.split)
+    launch_timed(attention_mfma_kernel<DT, D, kModeSplit>, dim3(grid), dim3(kAttnThreads), s, a);
+  else if (a.prefix_parts > 0)
+    launch_timed(attention_mfma_kernel<DT, D, kModePrefix>, dim3(grid), dim3(kAttnThreads), s, a);
   else
-    return hipErrorInvalidValue;
+    launch_timed(attention_mfma_kernel<DT, D, kModePlain>, dim3(grid), dim3(kAttnThreads), s, a);
   return hipGetLastError();
 }
 
 template <Dt DT>
-int attention_mfma_blocks_per_cu(int d_head) {
-  int n = 0;
-  if (d_head == 64)
-    (void)hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, attention_mfma_kernel<DT, 64>,
-                                                       kAttnThreads, 0);
-  else
-    (void)hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, attention_mfma_kernel<DT, 128>,
-                                                       kAttnThreads, 0);
+hipError_t launch_attention_mfma(const AttnArgs& a, int d_head, unsigned grid, hipStream_t s) {
+  if (d_head == 64) return launch_attention_mfma_d<DT, 64>(a, grid, s);
+  if (d_head == 128) return launch_attention_mfma_d<DT, 128>(a, grid, s);
+  return hipErrorInvalidValue;
+}
+
+// Work groups per CU, the fewest over the three modes (all are built for two).
+template <Dt DT, int D>
+int attention_mfma_blocks_per_cu_d() {
+  int n = 1 << 30;
+  for (int m = 0; m < 3; ++m) {
+    int k = 0;
+    (void)hipOccupancyMaxActiveBlocksPerMultiprocessor(
+        &k,
+        m == 0 ? attention_mfma_kernel<DT, D, kModePlain>
+               : m == 1 ? attention_mfma_kernel<DT, D, kModePrefix>
+                        : attention_mfma_kernel<DT, D, kModeSplit>,
+        kAttnThreads, 0);
+    n = std::min(n, k);
+  }
   return n > 0 ? n : 1;
+}
+
+template <Dt DT>
+int attention_mfma_blocks_per_cu(int d_head) {
+  return d_head == 64 ? attention_mfma_blocks_per_cu_d<DT, 64>()
+                      : attention_mfma_blocks_per_cu_d<DT, 128>();
 }
 
 }  // namespace pa
