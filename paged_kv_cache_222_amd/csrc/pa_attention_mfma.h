@@ -669,6 +669,30 @@ __global__ __launch_bounds__(kAttnThreads, PA_MFMA_MIN_BLOCKS) void attention_mf
     t0 = __builtin_amdgcn_readfirstlane(t0);
     t1 = __builtin_amdgcn_readfirstlane(t1);
     const int ntile = (t1 - t0 + 15) >> 4;
+    // Shared items: the pairs (sequence bseq + sq, block j of the item), sq
+    // >= 1, numbered idx = (sq - 1) * nbi + j; thread t loads the first
+    // sequence's and sequence sq's entries of pairs t and t + 256 here, after
+    // the queries and before the first tile's copies, so the wait for that
+    // tile (loads complete in issue order) covers them and nothing in the
+    // tile loop waits for them; they are compared after the loop.  Pairs
+    // past 512 (only with more than 512 / nbi sequences per item) are
+    // compared there too, loaded then.
+    int mis_e0[2] = {0, 0}, mis_e1[2] = {0, 0};
+    int nbi = 0, n_pairs = 0;
+    const int32_t* mis_row = a.block_table + (int64_t)bseq * a.max_blocks + (t0 >> a.block_shift);
+    if (pre) {
+      nbi = (t1 - t0 + bs - 1) >> a.block_shift;
+      n_pairs = (nq_valid - 1) * nbi;
+#pragma unroll
+      for (int k = 0; k < 2; ++k) {
+        const int idx = threadIdx.x + k * kAttnThreads;
+        if (idx < n_pairs) {
+          const int sq = 1 + idx / nbi, j = idx - (sq - 1) * nbi;
+          mis_e0[k] = mis_row[j];
+          mis_e1[k] = mis_row[(int64_t)sq * a.max_blocks + j];
+        }
+      }
+    }
     // The folded cache write (decode only): the work item holding position
     // ctx - 1 -- the sequence's final partition -- stores the new row of its
     // KV head in the pool, and the wave that owns that position's tile
@@ -697,9 +721,10 @@ __global__ __launch_bounds__(kAttnThreads, PA_MFMA_MIN_BLOCKS) void attention_mf
     char* my_ring = s_ring + wave * 4 * TILE;  // slot x: K at 2x*TILE, V at (2x+1)*TILE
     bool bad = false;
     // A shared item reads the first sequence's table for the whole group:
-    // bit s is set when sequence bseq + s names other blocks for a tile of
-    // the item (the rows do not share the prefix as stated), and that
-    // sequence's columns are written as NaN.
+    // bit s is set when sequence bseq + s names other blocks for the item's
+    // positions (the rows do not share the prefix as stated), and that
+    // sequence's columns are written as NaN.  The entries are loaded at the
+    // item's start (see mis_load) and compared after its tiles.
     uint32_t mis = 0u;
 
     // Byte offsets (in a KV head's view of a pool) of a tile's rows 0-7 and
@@ -721,12 +746,6 @@ __global__ __launch_bounds__(kAttnThreads, PA_MFMA_MIN_BLOCKS) void attention_mf
       const bool ok0 = p0 >= 0 && p0 < a.n_blocks;
       const bool ok1 = p1 >= 0 && p1 < a.n_blocks;
       bad |= !(ok0 && ok1);
-      if (pre) {
-        for (int sq = 1; sq < nq_valid; ++sq) {
-          const __attribute__((address_space(4))) int32_t* orow = trow + (int64_t)sq * a.max_blocks;
-          if (orow[bl0] != p0 || orow[bl1] != p1) mis |= 1u << sq;
-        }
-      }
       TileBase t;
       t.lo = (ok0 ? (int64_t)p0 : 0) * blk_bytes + (int64_t)(tok & (bs - 1)) * RB;
       t.hi = (ok1 ? (int64_t)p1 : 0) * blk_bytes + (int64_t)(tok_hi & (bs - 1)) * RB - 8 * RB;
@@ -892,6 +911,22 @@ __global__ __launch_bounds__(kAttnThreads, PA_MFMA_MIN_BLOCKS) void attention_mf
         patch_new_row(i + 1, 1);
         compute(i + 1, std::integral_constant<int, 1>{});
       }
+    }
+
+    if (pre) {
+      uint32_t lm = 0u;
+#pragma unroll
+      for (int k = 0; k < 2; ++k) {
+        const int idx = threadIdx.x + k * kAttnThreads;
+        if (idx < n_pairs && mis_e0[k] != mis_e1[k]) lm |= 1u << (1 + idx / nbi);
+      }
+      for (int idx = threadIdx.x + 2 * kAttnThreads; idx < n_pairs; idx += kAttnThreads) {
+        const int sq = 1 + idx / nbi, j = idx - (sq - 1) * nbi;
+        if (mis_row[j] != mis_row[(int64_t)sq * a.max_blocks + j]) lm |= 1u << sq;
+      }
+#pragma unroll
+      for (int d = 1; d < kWave; d <<= 1) lm |= (uint32_t)shfl_xor_i((int)lm, d);
+      mis = __builtin_amdgcn_readfirstlane(lm);
     }
 
     // ---- merge the waves
