@@ -68,9 +68,10 @@ def parse():
                                           "partitioned", "single", "prefix",
                                           "vector"],
                     default="all",
-                    help="all (default): time every form, report the fused "
-                         "step (the shared-prefix step for a batch with a "
-                         "shared prefix); best: report the fastest form; "
+                    help="all (default): time every form, report the "
+                         "batch's headline form (HEADLINE_FORM; the "
+                         "shared-prefix step for a batch with a shared "
+                         "prefix); best: report the fastest form; "
                          "vector: the partitioned form on the vector-ALU "
                          "kernel (pa_decode_partitioned_vector), timed only "
                          "when asked for")
@@ -120,7 +121,7 @@ def algorithmic_bytes(w):
 # form measured on MI355X for that batch (a batch with a shared prefix
 # reports "prefix").
 HEADLINE_FORM = {"llama3-8b": "fused", "qwen2.5-1.5b": "fused",
-                 "llama2-7b": "fused", "tiny": "fused"}
+                 "llama2-7b": "single", "tiny": "fused"}
 
 # sources whose change invalidates the HBM byte counts stored under profiles/
 KERNEL_SOURCES = ["pa_attention_mfma.h", "pa_attention_mfma.hip",
