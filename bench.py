@@ -140,33 +140,31 @@ def kernel_source_hash():
 
 
 def measured_traffic(name, variant, P, block_size):
-    """HBM bytes per attention launch from the counter summary stored under
+    """HBM bytes per attention launch from a counter summary stored under
     profiles/ (FETCH_SIZE + WRITE_SIZE, each scaled by the copy-kernel
-    factor), or None when there is none for this workload or the kernel
-    sources changed since it was taken."""
+    factor) for this workload, form, partition and block size, or None when
+    there is none or the kernel sources changed since it was taken."""
     kernel = "attention_vector" if variant == "vector" else "attention_mfma"
-    path = os.path.join(ROOT, "profiles",
-                        f"{kernel}_{name}_P{P}_hbm_counters.txt")
-    if not os.path.exists(path):
-        path = os.path.join(ROOT, "profiles",
-                            f"{kernel}_{name}_hbm_counters.txt")
-    if not os.path.exists(path):
-        return None
-    kv = {}
-    with open(path) as fh:
-        for line in fh:
-            if ":" in line and not line.startswith((" ", "#", "\t")):
-                k, v = line.split(":", 1)
-                kv[k.strip()] = v.strip()
-    if (kv.get("source_sha256_16") != kernel_source_hash()
-            or kv.get("variant") != variant
-            or kv.get("partition_size") != str(P)
-            or kv.get("block_size", "16") != str(block_size)):
-        return None
-    try:
-        return int(kv["traffic_bytes_per_launch"])
-    except (KeyError, ValueError):
-        return None
+    for fname in (f"{kernel}_{name}_P{P}_hbm_counters.txt",
+                  f"{kernel}_{name}_hbm_counters.txt"):
+        path = os.path.join(ROOT, "profiles", fname)
+        if not os.path.exists(path):
+            continue
+        kv = {}
+        with open(path) as fh:
+            for line in fh:
+                if ":" in line and not line.startswith((" ", "#", "\t")):
+                    k, v = line.split(":", 1)
+                    kv[k.strip()] = v.strip()
+        if (kv.get("source_sha256_16") == kernel_source_hash()
+                and kv.get("variant") == variant
+                and kv.get("partition_size") == str(P)
+                and kv.get("block_size", "16") == str(block_size)):
+            try:
+                return int(kv["traffic_bytes_per_launch"])
+            except (KeyError, ValueError):
+                return None
+    return None
 
 
 def n_copies(args, w):
@@ -199,10 +197,13 @@ def measure_read_ceiling(torch, pa, gib=4, reps=10, batch_tiles=0):
     """The device's achievable HBM read rate for the attention kernels'
     access pattern: pa_read_ceiling over a ``gib`` GiB buffer, in address
     order and as a gather of its 4 KiB tiles in a random order (median of
-    ``reps`` launches timed with HIP events on torch's current stream, the
-    stream the launches go to).  With ``batch_tiles``, also the gather of
-    only that many tiles -- as many bytes as one decode step reads -- whose
-    rate includes the start and end of a launch of that size."""
+    ``reps`` launches, each timed by its own dispatch's timestamps through
+    pa_time_next_attention, on torch's current stream, the stream the
+    launches go to).  With ``batch_tiles``, also the gather of only that many
+    tiles -- as many bytes as one decode step reads -- whose rate includes
+    the start and end of a launch of that size; its launches rotate over
+    disjoint sets of tiles (at least 3, as the decode steps rotate over input
+    copies) so that no launch finds its tiles in the last-level cache."""
     nbytes = gib << 30
     buf = torch.zeros(nbytes // 4, dtype=torch.int32, device="cuda")
     n_tiles = nbytes // 4096
@@ -210,26 +211,31 @@ def measure_read_ceiling(torch, pa, gib=4, reps=10, batch_tiles=0):
     order = torch.randperm(n_tiles, generator=gen).to(torch.int32).cuda()
     sink = torch.zeros(1, dtype=torch.int32, device="cuda")
     res = {"buffer_bytes": nbytes, "tile_bytes": 4096}
-    legs = [("stream", {}), ("tile_gather", {"tile_order": order})]
+    legs = [("stream", [{}]), ("tile_gather", [{"tile_order": order}])]
     if batch_tiles:
-        legs.append(("batch_size_tile_gather",
-                     {"tile_order": order, "n_tiles": int(batch_tiles)}))
-    for name, kw in legs:
-        for _ in range(2):
+        nb = int(batch_tiles)
+        sets = min(8, n_tiles // nb)
+        if sets >= 3:
+            legs.append(("batch_size_tile_gather",
+                         [{"tile_order": order[k * nb:(k + 1) * nb]}
+                          for k in range(sets)]))
+            res["batch_size_tile_sets"] = sets
+    for name, kws in legs:
+        for kw in kws[:2]:
             pa.pa_read_ceiling(buf, sink, **kw)
         torch.cuda.synchronize()
         ts = []
-        for _ in range(reps):
+        for r in range(reps):
             e0, e1 = (torch.cuda.Event(enable_timing=True) for _ in range(2))
-            e0.record()
-            pa.pa_read_ceiling(buf, sink, **kw)
-            e1.record()
+            pa.pa_time_next_attention(e0, e1)
+            pa.pa_read_ceiling(buf, sink, **kws[(r + 2) % len(kws)])
             torch.cuda.synchronize()
             ts.append(e0.elapsed_time(e1))
         ms = float(np.median(ts))
-        moved = nbytes if "n_tiles" not in kw else kw["n_tiles"] * 4096
+        moved = (kws[0]["tile_order"].numel() * 4096
+                 if name == "batch_size_tile_gather" else nbytes)
         res[f"{name}_GBs"] = round(moved / (ms * 1e-3) / 1e9, 1)
-        if "n_tiles" in kw:
+        if name == "batch_size_tile_gather":
             res[f"{name}_bytes"] = moved
             res[f"{name}_us"] = round(ms * 1e3, 2)
     del buf, order
@@ -824,8 +830,9 @@ def main():
         rc = measure_read_ceiling(torch, pa, batch_tiles=uniq // 4096)
         rc["attention_frac_of_tile_gather"] = round(
             achieved / rc["tile_gather_GBs"], 4)
-        rc["attention_frac_of_batch_size_gather"] = round(
-            achieved / rc["batch_size_tile_gather_GBs"], 4)
+        if "batch_size_tile_gather_GBs" in rc:
+            rc["attention_frac_of_batch_size_gather"] = round(
+                achieved / rc["batch_size_tile_gather_GBs"], 4)
         rec["read_ceiling"] = rc
     if not args.no_cpu_baseline:
         log("timing the fp64 CPU oracle on a sample")

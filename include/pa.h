@@ -144,8 +144,10 @@ int pa_read_ceiling(const void* buf, int64_t buf_bytes, const int32_t* tile_orde
 /*
  * pa_time_next_attention -- a measurement aid, not part of the decode path:
  * the attention kernel launched next by a decode call on this thread (any
- * of pa_decode, pa_decode_partitioned, pa_decode_step, pa_decode_split,
- * pa_decode_shared_prefix, pa_decode_multi) records its own start in
+ * of pa_decode, pa_decode_partitioned, pa_decode_partitioned_vector,
+ * pa_decode_step, pa_decode_split, pa_decode_shared_prefix,
+ * pa_decode_multi), or the read kernel of the next pa_read_ceiling call,
+ * records its own start in
  * start_event and its end in stop_event (hipEvent_t handles the caller
  * created with timing enabled; either may be NULL).  hipEventElapsedTime
  * of the two is then the kernel's execution time, without the gaps between

@@ -52,7 +52,7 @@ __global__ __launch_bounds__(kReadThreads) void read_ceiling_kernel(ReadCeilingA
 }
 
 hipError_t launch_read_ceiling(const ReadCeilingArgs& a, unsigned grid, hipStream_t s) {
-  hipLaunchKernelGGL(read_ceiling_kernel, dim3(grid), dim3(kReadThreads), 0, s, a);
+  launch_timed(read_ceiling_kernel, dim3(grid), dim3(kReadThreads), s, a);
   return hipGetLastError();
 }
 

@@ -74,3 +74,22 @@ def test_gather_of_many_tiles_in_random_order(pa):
     pa.pa_read_ceiling(buf, sink, tile_order=order)
     torch.cuda.synchronize()
     assert _bits(sink) == MAGIC
+
+
+def test_timing_events_bracket_the_read_kernel(pa):
+    """pa_time_next_attention also times the next pa_read_ceiling launch:
+    its events come back recorded, the interval inside the one measured by
+    events around the call, and consumed by that launch."""
+    buf = _buffer(20000, 7)
+    sink = _sink()
+    outer0, outer1, k0, k1 = (torch.cuda.Event(enable_timing=True)
+                              for _ in range(4))
+    note("pa_read_ceiling with dispatch-timestamp events")
+    outer0.record()
+    pa.pa_time_next_attention(k0, k1)
+    pa.pa_read_ceiling(buf, sink)
+    outer1.record()
+    torch.cuda.synchronize()
+    inner = k0.elapsed_time(k1)
+    assert 0.0 < inner <= outer0.elapsed_time(outer1) + 1e-3
+    assert _bits(sink) == MAGIC
