@@ -16,10 +16,14 @@
  * Conventions for every entry point
  * ---------------------------------
  * - Pointers are DEVICE pointers owned by the caller unless stated otherwise.
- *   The GPU entry points never allocate, free or retain memory.  The only
- *   state they keep is a per-device note of how many work groups fit on the
- *   device (filled on first use, thread-safe), so calls on different
- *   streams or threads are independent.
+ *   The GPU entry points never allocate or free memory.  State they keep:
+ *   a note of how many work groups fit on each of the first 64 devices
+ *   (filled on first use, thread-safe; later devices are queried on every
+ *   call); the fixed device array of pa_decode_step_noalloc (one per device,
+ *   shared by that entry point's calls, see there); and the two events set
+ *   by pa_time_next_attention, per host thread, until the launch that uses
+ *   them.  Apart from pa_decode_step_noalloc, calls on different streams or
+ *   threads are independent.
  *   The host-side block pool (pa_pool_*, pa_block_hashes, at the end) works
  *   on HOST memory: a pool is an object the caller creates and destroys.
  * - All arrays are dense and row-major, with the shapes given below, and
