@@ -148,8 +148,9 @@ def simulate(arrivals, prompt_lens, final_lens, n_blocks, block_size,
     tokens at step t until it holds ``final_lens[i]``: it finishes at
     f_i = s_i + final_lens[i] - prompt_lens[i] and frees its blocks after
     that step is counted.  Blocks held at step t ("Serving", section 23.4:
-    paging hands out blocks as a sequence grows; reserving takes the worst
-    case up front):
+    under paging a request gets one more block each time its tokens outgrow
+    the blocks it holds; under reservation it claims its worst case when it
+    starts):
 
     * ``"reserve"``: ceil(max_len / block_size) for every step of its life;
     * ``"paged"``: ceil(tokens(t) / block_size).
