@@ -86,14 +86,16 @@ def parse():
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
                     help="budget of the CPU oracle sample")
     ap.add_argument("--op", choices=["decode", "copy-blocks", "verify",
-                                     "prefix-cache"],
+                                     "prefix-cache", "timeline"],
                     default="decode",
                     help="decode: the decode step (default); copy-blocks: "
                          "the copy-on-write block copy on the LLaMA-3-8B pool; "
                          "verify: a speculative-decoding verify step, "
                          "--queries tokens per sequence; prefix-cache: the "
                          "host-side block hashes and prefix mapping of the "
-                         "shared-prefix batch (no GPU)")
+                         "shared-prefix batch (no GPU); timeline: per-work-"
+                         "group timeline of the attention kernel (a library "
+                         "built with -DPA_TIMELINE, named by PA_LIBRARY)")
     ap.add_argument("--queries", type=int, default=4,
                     help="verify: query tokens per sequence")
     ap.add_argument("--pairs", type=int, default=4096,
@@ -460,6 +462,142 @@ def bench_verify(args, torch, pa, wl):
     print(json.dumps(rec), flush=True)
 
 
+def bench_timeline(args, torch, pa, wl):
+    """Per-work-group timeline of the matrix-core attention kernel, from a
+    library built with -DPA_TIMELINE (python -m
+    paged_kv_cache_222_amd.build --out=PATH -DPA_TIMELINE; PA_LIBRARY=PATH):
+    thread 0 of every work group records s_memrealtime (100 MHz) at its
+    start, after the plan and around every item.  Runs --warmup launches,
+    then --steps recorded launches of the batch's form (--variant fused,
+    split, partitioned or prefix), each on its own resident input copy, and
+    prints the summary of each and one JSON line with the last."""
+    import ctypes
+    lib = pa.load()
+    if not hasattr(lib, "pa_timeline_copy"):
+        sys.exit("--op timeline needs a library built with -DPA_TIMELINE "
+                 "(python -m paged_kv_cache_222_amd.build --out=PATH "
+                 "-DPA_TIMELINE), named by PA_LIBRARY")
+    lib.pa_timeline_copy.argtypes = [ctypes.c_void_p, ctypes.c_size_t]
+    lib.pa_timeline_copy.restype = ctypes.c_int
+    lib.pa_timeline_clear.restype = ctypes.c_int
+    n_groups, n_slots, n_items = 4096, 64, 18
+    kw = {"block_size": args.block_size} if args.block_size else {}
+    w = wl.make_workload(args.config, seed=args.seed, **kw)
+    c = w.cfg
+    P = args.partition_size or c.partition_size
+    form = args.variant if args.variant in ("fused", "split", "partitioned",
+                                            "prefix") else (
+        "prefix" if c.prefix_len else "fused")
+    tdt = {"f16": torch.float16, "bf16": torch.bfloat16}[c.dtype]
+
+    def up(x, dt=None):
+        if dt is not None:
+            return torch.from_numpy(x.view(np.int16)).view(dt).cuda()
+        return torch.from_numpy(np.ascontiguousarray(x)).cuda()
+
+    copies = [dict(k=up(w.k_pool, tdt), v=up(w.v_pool, tdt))
+              for _ in range(n_copies(args, w))]
+    q, kn, vn = up(w.q, tdt), up(w.key_new, tdt), up(w.value_new, tdt)
+    tbl, cl = up(w.block_table), up(w.context_lens)
+    if form == "split":
+        pm = args.slots or split_slots(w, torch)
+    else:
+        pm = max(1, -(-int(w.context_lens.max()) // P))
+    ws = pa.partition_workspace(c.batch, c.n_q_heads, c.d_head, pm)
+
+    def launch(x):
+        if form == "fused":
+            pa.pa_decode_step(*ws, kn, vn, q, x["k"], x["v"], tbl, cl,
+                              partition_size=P, scale=w.scale)
+        elif form == "split":
+            pa.pa_decode_split(*ws, q, x["k"], x["v"], tbl, cl, scale=w.scale,
+                               key_new=kn, value_new=vn)
+        elif form == "prefix":
+            pa.pa_decode_shared_prefix(*ws, q, x["k"], x["v"], tbl, cl,
+                                       partition_size=P,
+                                       prefix_len=c.prefix_len, scale=w.scale,
+                                       key_new=kn, value_new=vn)
+        else:
+            pa.pa_decode_partitioned(*ws, q, x["k"], x["v"], tbl, cl,
+                                     partition_size=P, scale=w.scale)
+
+    for i in range(args.warmup):
+        launch(copies[i % len(copies)])
+    torch.cuda.synchronize()
+    runs = []
+    for i in range(args.steps):
+        if lib.pa_timeline_clear() != 0:
+            sys.exit("pa_timeline_clear failed")
+        torch.cuda.synchronize()
+        launch(copies[i % len(copies)])
+        torch.cuda.synchronize()
+        buf = np.zeros(n_groups * n_slots, dtype=np.uint64)
+        if lib.pa_timeline_copy(buf.ctypes.data, buf.nbytes) != 0:
+            sys.exit("pa_timeline_copy failed")
+        runs.append(buf.reshape(n_groups, n_slots).astype(np.int64))
+
+    def summary(t):
+        t = t[t[:, 0] > 0]
+        t0 = t[:, 0].min()
+        us = lambda x: (x - t0) / 100.0           # 100 MHz ticks
+        st, pl, en = us(t[:, 0]), us(t[:, 1]), us(t[:, 2])
+        nit = t[:, 3]
+        xcc = (t[:, 60] >> 32) & 0xF
+        hw = t[:, 60] & 0xFFFFFFFF
+        # HW_ID: CU id bits 8-11, shader array bit 12, shader engine 13-15
+        cu_key = xcc * 256 + ((hw >> 8) & 0xFF)
+        firsts, seconds = [], []
+        for key in np.unique(cu_key):
+            idx = np.where(cu_key == key)[0]
+            if len(idx) == 2:
+                i0, i1 = idx[np.argsort(st[idx])]
+                firsts.append(en[i0])
+                seconds.append(en[i1])
+        durs, tiles, gaps = [], [], []
+        for g in range(len(t)):
+            prev = None
+            for k in range(min(n_items, int(nit[g]))):
+                s0, s1, info = t[g, 4 + 3 * k], t[g, 5 + 3 * k], t[g, 6 + 3 * k]
+                durs.append((s1 - s0) / 100.0)
+                tiles.append(info & 0xFFFFF)
+                if prev is not None:
+                    gaps.append((s0 - prev) / 100.0)
+                prev = s1
+        fit = [None, None]
+        if len(durs) > 2 and np.ptp(tiles) > 0:
+            A = np.vstack([np.ones(len(tiles)), np.array(tiles, float)]).T
+            fit = [round(float(x), 3) for x in
+                   np.linalg.lstsq(A, np.array(durs), rcond=None)[0]]
+        return {
+            "work_groups": int(len(t)),
+            "span_us": round(float(en.max()), 2),
+            "start_us_p50_max": [round(float(np.median(st)), 2),
+                                 round(float(st.max()), 2)],
+            "plan_end_after_start_us_p50": round(float(np.median(pl - st)), 2),
+            "end_us_p0_p10_p50_p90_max": [round(float(x), 1) for x in
+                                          np.percentile(en, [0, 10, 50, 90, 100])],
+            "items_per_group_mean_max": [round(float(nit.mean()), 2),
+                                         int(nit.max())],
+            "xcc_median_end_us": [round(float(np.median(en[xcc == x])), 1)
+                                  for x in range(8) if (xcc == x).any()],
+            "cu_pairs": len(firsts),
+            "cu_pair_end_us_first_second_p50":
+                [round(float(np.median(firsts)), 1),
+                 round(float(np.median(seconds)), 1)] if firsts else None,
+            "item_us_fixed_per_tile": fit,
+            "gap_between_items_us_p50":
+                round(float(np.median(gaps)), 2) if gaps else None,
+        }
+
+    for i, t in enumerate(runs):
+        log(f"launch {i}: {json.dumps(summary(t))}")
+    print(json.dumps({"op": "timeline", "config": c.name, "form": form,
+                      "partition_size": P if form != "split" else None,
+                      "slots": pm, "launches": len(runs),
+                      "spans_us": [summary(t)["span_us"] for t in runs],
+                      "last": summary(runs[-1])}), flush=True)
+
+
 def bench_prefix_cache(args):
     """Host-side prefix caching on the shared-prefix batch: each of the 256
     requests (a 2048-token shared prompt + a private suffix U[1, 6144], token
@@ -618,6 +756,9 @@ def main():
         return
     if args.op == "verify":
         bench_verify(args, torch, pa, wl)
+        return
+    if args.op == "timeline":
+        bench_timeline(args, torch, pa, wl)
         return
     kw = {}
     if args.block_size:

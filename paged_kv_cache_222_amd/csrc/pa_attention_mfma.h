@@ -46,6 +46,32 @@
 
 namespace pa {
 
+// A timeline of every work group, in a measurement build only (built with
+// -DPA_TIMELINE; bench.py --op timeline reads it): thread 0 of work group g
+// stores 64-bit words at g * kTimelineSlots + slot of g_timeline, with
+// vector stores -- slot 0 the start (s_memrealtime, a 100 MHz counter), 1
+// the end of the plan, 2 the end, 3 the number of items completed, 60 the
+// XCC id << 32 | HW_ID, and for item k < kTimelineItems: 4 + 3k its start,
+// 5 + 3k its end, 6 + 3k its tiles | shared << 20 | sequence << 32.  In the
+// product build the macros are empty.
+constexpr int kTimelineGroups = 4096;
+constexpr int kTimelineSlots = 64;
+constexpr int kTimelineItems = 18;
+#ifdef PA_TIMELINE
+__device__ unsigned long long g_timeline[kTimelineGroups * kTimelineSlots];
+#define PA_TL(slot, v)                                                        \
+  do {                                                                        \
+    if (threadIdx.x == 0 && blockIdx.x < kTimelineGroups)                     \
+      g_timeline[blockIdx.x * kTimelineSlots + (slot)] = (unsigned long long)(v); \
+  } while (0)
+#define PA_TL_NOW() __builtin_amdgcn_s_memrealtime()
+#else
+#define PA_TL(slot, v) \
+  do {                 \
+  } while (0)
+#define PA_TL_NOW() 0ull
+#endif
+
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef _Float16 f16x8_t __attribute__((ext_vector_type(8)));
 typedef short s16x4_t __attribute__((ext_vector_type(4)));
@@ -242,6 +268,15 @@ __global__ __launch_bounds__(kAttnThreads, PA_MFMA_MIN_BLOCKS) void attention_mf
   int* s_rank = s_key + kPlanMaxBatch;
   static_assert(2 * kPlanMaxBatch * 4 <= NW * 4 * TILE, "plan keys must fit the rings");
 
+  PA_TL(0, PA_TL_NOW());
+#ifdef PA_TIMELINE
+  {
+    // hardware register ids 20 (XCC_ID) and 4 (HW_ID), 16 and 32 bits
+    const unsigned xcc = __builtin_amdgcn_s_getreg(20 | (0 << 6) | (15 << 11));
+    const unsigned hw = __builtin_amdgcn_s_getreg(4 | (0 << 6) | (31 << 11));
+    PA_TL(60, ((unsigned long long)xcc << 32) | hw);
+  }
+#endif
   const int lane = threadIdx.x & (kWave - 1);
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
   const int l16 = lane & 15;
@@ -468,6 +503,9 @@ __global__ __launch_bounds__(kAttnThreads, PA_MFMA_MIN_BLOCKS) void attention_mf
     n_items = K * a.batch;   // single pass, or a split launch without the plan
   }
 
+  PA_TL(1, PA_TL_NOW());
+  int tl_k = 0;   // items completed (timeline build)
+  (void)tl_k;
   const float sl2 = a.scale_log2;
   const float qnan = __builtin_nanf("");
   float* s_o = reinterpret_cast<float*>(s_ring);  // [NW][16][D] after the tiles
@@ -508,6 +546,7 @@ __global__ __launch_bounds__(kAttnThreads, PA_MFMA_MIN_BLOCKS) void attention_mf
       kh = item % K;
       rr = item / K;
     }
+    if (tl_k < kTimelineItems) PA_TL(4 + 3 * tl_k, PA_TL_NOW());
     const int kvh = kh / a.n_hchunks;
     const int hc = kh - kvh * a.n_hchunks;
     // pre: a shared-prefix item; b is then the group of sequences
@@ -1047,7 +1086,15 @@ __global__ __launch_bounds__(kAttnThreads, PA_MFMA_MIN_BLOCKS) void attention_mf
       }
     }
     lds_barrier();  // the merge buffer is the next item's rings
+    if (tl_k < kTimelineItems) {
+      PA_TL(5 + 3 * tl_k, PA_TL_NOW());
+      PA_TL(6 + 3 * tl_k, (unsigned long long)ntile | ((unsigned long long)pre << 20) |
+                              ((unsigned long long)(unsigned)b << 32));
+    }
+    ++tl_k;
   }
+  PA_TL(2, PA_TL_NOW());
+  PA_TL(3, tl_k);
 }
 
 template <Dt DT, int D>

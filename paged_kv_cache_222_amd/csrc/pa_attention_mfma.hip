@@ -19,3 +19,21 @@ int attention_mfma_occupancy(int dtype, int d_head) {
 }
 
 }  // namespace pa
+
+#ifdef PA_TIMELINE
+// The timeline's host side (measurement build only; not in include/pa.h).
+extern "C" int pa_timeline_copy(void* dst, size_t bytes) {
+  if (bytes > sizeof(pa::g_timeline)) return -2;
+  return hipMemcpyFromSymbol(dst, HIP_SYMBOL(pa::g_timeline), bytes, 0, hipMemcpyDeviceToHost) ==
+                 hipSuccess
+             ? 0
+             : -1;
+}
+extern "C" int pa_timeline_clear() {
+  static unsigned long long zero[pa::kTimelineGroups * pa::kTimelineSlots];
+  return hipMemcpyToSymbol(HIP_SYMBOL(pa::g_timeline), zero, sizeof(zero), 0,
+                           hipMemcpyHostToDevice) == hipSuccess
+             ? 0
+             : -1;
+}
+#endif
