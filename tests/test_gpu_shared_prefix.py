@@ -332,6 +332,38 @@ def test_rows_not_sharing_the_prefix_get_nan(pa):
             assert (np.abs(got[b] - ref[b]) <= out_bound(ref[b], "bf16")).all(), b
 
 
+def test_mismatch_past_the_first_512_pairs_is_found(pa):
+    """G = 1 puts 16 sequences in a shared item; with blocks of 8 and 1024-
+    position partitions an item has 15 x 128 = 1920 (sequence, block) pairs
+    to check, past the two per thread the item keeps in registers.
+    Sequence 2 differs at block 10 of partition 0 (pair 138) and sequence 15
+    at its last block (pair 1919): both NaN, every other row the oracle's."""
+    bs, P, plen = 8, 1024, 2048
+    ctx = [plen + 1 + 8 * (i % 5) + i for i in range(18)]
+    w = wl.make_custom(ctx, n_q_heads=2, n_kv_heads=2, d_head=128,
+                       block_size=bs, dtype="bf16", seed=61,
+                       prefix_len=plen,
+                       pool_blocks=sum(-(-c // bs) for c in ctx)
+                       - (plen // bs) * (len(ctx) - 1) + 16)
+    free = sorted(set(range(w.n_blocks)) -
+                  set(w.block_table[w.block_table >= 0].tolist()))
+    for s, j, fb in ((2, 10, free[0]), (15, P // bs - 1, free[1])):
+        src = int(w.block_table[s, j])
+        w.k_pool[fb] = w.k_pool[src]
+        w.v_pool[fb] = w.v_pool[src]
+        w.block_table[s, j] = fb
+    d = DeviceBatch(w)
+    out, _ = _run(pa, d, P, plen, write=True, name="mismatch past 512 pairs")
+    k_ref, v_ref = oracle_pools_after_write(w)
+    ref = oracle_out(w, k_ref, v_ref)
+    got = as_f64(out)
+    for b in range(len(ctx)):
+        if b in (2, 15):
+            assert np.isnan(got[b]).all(), b
+        else:
+            assert (np.abs(got[b] - ref[b]) <= out_bound(ref[b], "bf16")).all(), b
+
+
 def test_private_copy_outside_shared_items_is_correct(pa):
     """A row that points a prefix block at a copy outside every shared
     partition reads it through its own table: the oracle's result."""
