@@ -568,12 +568,20 @@ def bench_timeline(args, torch, pa, wl):
             A = np.vstack([np.ones(len(tiles)), np.array(tiles, float)]).T
             fit = [round(float(x), 3) for x in
                    np.linalg.lstsq(A, np.array(durs), rcond=None)[0]]
+        phases = None
+        if (t[:, 58] > 0).all() and (t[:, 61] > 0).all():
+            # plan phases after a work group's start (p50): context lengths
+            # in, after the scans, after the rank, the plan's end
+            phases = [round(float(np.median(us(t[:, k]) - st)), 2)
+                      for k in (58, 59, 61)] + \
+                     [round(float(np.median(pl - st)), 2)]
         return {
             "work_groups": int(len(t)),
             "span_us": round(float(en.max()), 2),
             "start_us_p50_max": [round(float(np.median(st)), 2),
                                  round(float(st.max()), 2)],
             "plan_end_after_start_us_p50": round(float(np.median(pl - st)), 2),
+            "plan_phases_us_p50_lengths_scan_rank_end": phases,
             "end_us_p0_p10_p50_p90_max": [round(float(x), 1) for x in
                                           np.percentile(en, [0, 10, 50, 90, 100])],
             "items_per_group_mean_max": [round(float(nit.mean()), 2),

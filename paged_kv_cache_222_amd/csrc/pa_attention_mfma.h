@@ -52,8 +52,9 @@ namespace pa {
 // vector stores -- slot 0 the start (s_memrealtime, a 100 MHz counter), 1
 // the end of the plan, 2 the end, 3 the number of items completed, 60 the
 // XCC id << 32 | HW_ID, and for item k < kTimelineItems: 4 + 3k its start,
-// 5 + 3k its end, 6 + 3k its tiles | shared << 20 | sequence << 32.  In the
-// product build the macros are empty.
+// 5 + 3k its end, 6 + 3k its tiles | shared << 20 | sequence << 32; in the
+// partition plan also 58 (context lengths in), 59 (after the scans) and 61
+// (after the rank).  In the product build the macros are empty.
 constexpr int kTimelineGroups = 4096;
 constexpr int kTimelineSlots = 64;
 constexpr int kTimelineItems = 18;
@@ -425,12 +426,14 @@ __global__ __launch_bounds__(kAttnThreads, PA_MFMA_MIN_BLOCKS) void attention_mf
       fs += fl[j];
       ts += tl[j];
     }
+    PA_TL(58, PA_TL_NOW());   // thread 0 has its context lengths
     const int fi = wave_incl_scan(fs), ti = wave_incl_scan(ts);
     if (lane == kWave - 1) {
       s_m[wave][0] = __builtin_bit_cast(float, fi);
       s_l[wave][0] = __builtin_bit_cast(float, ti);
     }
     __syncthreads();
+    PA_TL(59, PA_TL_NOW());   // after the scans' barrier
     int fo = 0, ftot = 0, ttot = 0;
 #pragma unroll
     for (int w = 0; w < NW; ++w) {
@@ -483,6 +486,7 @@ __global__ __launch_bounds__(kAttnThreads, PA_MFMA_MIN_BLOCKS) void attention_mf
       }
     }
     __syncthreads();
+    PA_TL(61, PA_TL_NOW());   // after the rank's barrier
     int fx = fo + fi - fs;  // exclusive offset of b = 4t
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
