@@ -1,0 +1,67 @@
+"""bench.py's reporting helpers, on the CPU: the algorithmic bytes of a
+launch (the sum of the per-sequence terms, written out independently here),
+the number of resident input copies, and the lookup of stored HBM counters
+(matched on form, partition and block size; null once the kernel sources
+change)."""
+
+import os
+import sys
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+sys.path.insert(0, ROOT)
+
+import pytest  # noqa: E402
+
+import bench  # noqa: E402
+from paged_kv_cache_222_amd import workloads as wl  # noqa: E402
+
+
+@pytest.fixture(scope="module")
+def llama3():
+    return wl.make_workload("llama3-8b", seed=0)
+
+
+def test_algorithmic_bytes_of_the_llama3_batch(llama3):
+    """Per sequence-step: K and V rows of every KV head, the queries, the
+    used table entries and the context length.  Seed 0: sum(ctx) = 217,087."""
+    w = llama3
+    c = w.cfg
+    ctx = w.context_lens.astype(np.int64)
+    want = 0
+    for n in ctx:
+        want += 2 * int(n) * c.n_kv_heads * c.d_head * 2          # K and V
+        want += c.n_q_heads * c.d_head * 2                       # q
+        want += 4 * -(-int(n) // c.block_size)                   # table
+        want += 4                                                 # length
+    assert int(ctx.sum()) == 217087
+    assert bench.algorithmic_bytes(w) == want == 890291956
+
+
+def test_resident_copies_leave_the_last_level_cache(llama3):
+    class A:
+        copies = None
+    for name, want in (("llama3-8b", 3), ("qwen2.5-1.5b", 8), ("tiny", 16)):
+        w = llama3 if name == "llama3-8b" else wl.make_workload(name, seed=0)
+        n = bench.n_copies(A, w)
+        assert n == want, name
+        per = w.kv_bytes_unique() if w.cfg.prefix_len else w.kv_bytes_logical()
+        # at least 1 GiB of other K/V reads between two uses of a copy,
+        # unless capped (a batch too small to leave the cache)
+        assert n == 16 or (n - 1) * per >= (1 << 30), name
+    A.copies = 5
+    assert bench.n_copies(A, wl.make_workload("tiny", seed=0)) == 5
+
+
+def test_traffic_lookup_matches_form_and_sources(monkeypatch):
+    # the committed LLaMA-3 counters are for the fused form at P 3072, BS 16
+    got = bench.measured_traffic("llama3-8b", "fused", 3072, 16)
+    if got is not None:       # the sources match the stored hash
+        assert 890_000_000 < got < 910_000_000
+    assert bench.measured_traffic("llama3-8b", "split", 3072, 16) is None
+    assert bench.measured_traffic("llama3-8b", "fused", 2048, 16) is None
+    assert bench.measured_traffic("llama3-8b", "fused", 3072, 32) is None
+    assert bench.measured_traffic("no-such-batch", "fused", 3072, 16) is None
+    monkeypatch.setattr(bench, "kernel_source_hash", lambda: "0" * 16)
+    assert bench.measured_traffic("llama3-8b", "fused", 3072, 16) is None
