@@ -554,15 +554,25 @@ def bench_timeline(args, torch, pa, wl):
                 firsts.append(en[i0])
                 seconds.append(en[i1])
         durs, tiles, gaps = [], [], []
+        wg_tiles = np.zeros(len(t))
         for g in range(len(t)):
             prev = None
             for k in range(min(n_items, int(nit[g]))):
                 s0, s1, info = t[g, 4 + 3 * k], t[g, 5 + 3 * k], t[g, 6 + 3 * k]
                 durs.append((s1 - s0) / 100.0)
                 tiles.append(info & 0xFFFFF)
+                wg_tiles[g] += info & 0xFFFFF
                 if prev is not None:
                     gaps.append((s0 - prev) / 100.0)
                 prev = s1
+        # each CU's tiles (all its work groups' items, when every item was
+        # recorded) and its end (its last work group's)
+        cu_tiles, cu_end = [], []
+        if (nit <= n_items).all():
+            for key in np.unique(cu_key):
+                idx = np.where(cu_key == key)[0]
+                cu_tiles.append(wg_tiles[idx].sum())
+                cu_end.append(en[idx].max())
         fit = [None, None]
         if len(durs) > 2 and np.ptp(tiles) > 0:
             A = np.vstack([np.ones(len(tiles)), np.array(tiles, float)]).T
@@ -592,6 +602,10 @@ def bench_timeline(args, torch, pa, wl):
             "cu_pair_end_us_first_second_p50":
                 [round(float(np.median(firsts)), 1),
                  round(float(np.median(seconds)), 1)] if firsts else None,
+            "cu_tiles_min_max": [int(min(cu_tiles)), int(max(cu_tiles))]
+                                if cu_tiles else None,
+            "cu_end_tiles_corr": round(float(np.corrcoef(cu_tiles, cu_end)[0, 1]), 2)
+                                 if cu_tiles and np.ptp(cu_tiles) > 0 else None,
             "item_us_fixed_per_tile": fit,
             "gap_between_items_us_p50":
                 round(float(np.median(gaps)), 2) if gaps else None,

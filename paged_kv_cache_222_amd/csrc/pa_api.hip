@@ -87,34 +87,40 @@ pa::AttnArgs attention_args(const void* q, const void* k_pool, const void* v_poo
   return a;
 }
 
-// Work groups of the matrix-core kernel that fit on the whole device.  It
-// depends only on the device and the kernel, and an occupancy query per call
-// would cost more than a small decode step, so it is memoised per (device,
-// dtype, d_head) for devices 0 .. kMemoDevices - 1 in relaxed atomics
-// (concurrent first calls store the same value); other devices are queried
-// on every call.
+// CUs of the current device and work groups of the matrix-core kernel that
+// fit on one.  They depend only on the device and the kernel, and an
+// occupancy query per call would cost more than a small decode step, so
+// they are memoised per (device, dtype, d_head) for devices 0 ..
+// kMemoDevices - 1 in relaxed atomics (concurrent first calls store the same
+// value); other devices are queried on every call.
 constexpr int kMemoDevices = 64;
 
-int query_slots(int dev, int32_t dtype, int32_t d_head) {
+struct DeviceFit {
+  int cus;      // compute units
+  int per_cu;   // work groups of the kernel per CU
+};
+
+DeviceFit query_fit(int dev, int32_t dtype, int32_t d_head) {
   int cus = 0;
   if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
       cus < 1)
     cus = 256;
-  return cus * pa::attention_mfma_occupancy(dtype, d_head);
+  return DeviceFit{cus, std::min(pa::attention_mfma_occupancy(dtype, d_head), 255)};
 }
 
-int device_slots(int32_t dtype, int32_t d_head) {
-  static std::atomic<int> memo[kMemoDevices][2][2];
+DeviceFit device_fit(int32_t dtype, int32_t d_head) {
+  static std::atomic<int> memo[kMemoDevices][2][2];   // cus << 8 | per_cu
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess || dev < 0) dev = 0;
-  if (dev >= kMemoDevices) return query_slots(dev, dtype, d_head);
+  if (dev >= kMemoDevices) return query_fit(dev, dtype, d_head);
   std::atomic<int>& c = memo[dev][dtype == PA_F16 ? 0 : 1][d_head == 64 ? 0 : 1];
   int v = c.load(std::memory_order_relaxed);
   if (v == 0) {
-    v = query_slots(dev, dtype, d_head);
+    const DeviceFit f = query_fit(dev, dtype, d_head);
+    v = f.cus << 8 | f.per_cu;
     c.store(v, std::memory_order_relaxed);
   }
-  return v;
+  return DeviceFit{v >> 8, v & 255};
 }
 
 // fp16/bf16 run on the matrix cores (query heads in chunks of 16); fp32 on
@@ -138,7 +144,9 @@ hipError_t dispatch_attention(pa::AttnArgs a, int32_t dtype, int32_t d_head, int
   const int64_t cols = (int64_t)a.n_kv_heads * a.n_hchunks;
   int64_t grid = rows * cols;
   a.persistent = 0;
-  const int64_t slots = device_slots(dtype, d_head);
+  a.cu_deal = 0;
+  const DeviceFit fit = device_fit(dtype, d_head);
+  const int64_t slots = (int64_t)fit.cus * fit.per_cu;
   if ((a.partition_size > 0 || a.split) && a.batch <= pa::kPlanBatch && slots >= cols) {
     // a whole number of work groups per column (KV head and head chunk); a
     // split launch fills the device whatever the batch
@@ -154,6 +162,11 @@ hipError_t dispatch_attention(pa::AttnArgs a, int32_t dtype, int32_t d_head, int
     a.prefix_parts = 0;
     a.prefix_seqs = 0;
   }
+  // Items dealt over CUs: the grid fills two work groups on every CU and a
+  // CU's two work groups are in one column.  Not with shared items: on the
+  // shared-prefix batch (31 items per work group) it cost 4 us at P 512.
+  a.cu_deal = a.persistent && !a.split && a.prefix_parts == 0 && fit.per_cu == 2 &&
+              grid == slots && (grid / cols) % 2 == 0;
   if (grid > INT_MAX || cols > INT_MAX) {
     *status = PA_ERR_SHAPE;
     return hipSuccess;

@@ -518,8 +518,16 @@ __global__ __launch_bounds__(kAttnThreads, PA_MFMA_MIN_BLOCKS) void attention_mf
   // head chunk), and work group j of a column takes its column's items
   // j, 2W-1-j, 2W+j, 4W-1-j, ... of the plan (full partitions, then final
   // partitions longest first): dealt back and forth, so the work groups of
-  // a column end with nearly equal loads.  Other launches take every
-  // gridDim.x-th (item, column) pair.
+  // a column end with nearly equal loads.  With cu_deal the grid is two
+  // work groups per CU, and work groups j and j + W/2 of a column share one
+  // (blocks b and b + gridDim.x/2 are dispatched to the same CU): the items
+  // are dealt back and forth over the W/2 CUs instead, the CU's rounds
+  // alternating between its two work groups.  The two work groups of a CU
+  // share its memory pipeline, so the CU's total sets its end: on the
+  // LLaMA-3-8B batch dealing over work groups left the CUs' totals 373-447
+  // tiles apart, dealing over CUs 406-436, and the launch went from 145.6
+  // to 143.9 us.  Other launches take every gridDim.x-th (item, column)
+  // pair.
   const int W = plan ? (int)gridDim.x / K : 0;
   const int jw = plan ? (int)blockIdx.x / K : 0;
   for (int it = 0;; ++it) {
@@ -542,7 +550,14 @@ __global__ __launch_bounds__(kAttnThreads, PA_MFMA_MIN_BLOCKS) void attention_mf
       n_pieces = (Sb + Tb - 1) / sp_R - Sb / sp_R + 1;
     } else if (plan) {
       kh = blockIdx.x % K;
-      rr = it * W + ((it & 1) ? W - 1 - jw : jw);
+      if (a.cu_deal) {
+        // round t of CU cu: position cu (t even) or C-1-cu (t odd); the
+        // CU's first work group takes its even rounds, the second its odd
+        const int C = W >> 1, cu = jw % C, t = 2 * it + jw / C;
+        rr = t * C + ((t & 1) ? C - 1 - cu : cu);
+      } else {
+        rr = it * W + ((it & 1) ? W - 1 - jw : jw);
+      }
       if (rr >= n_items) break;
     } else {
       const int item = blockIdx.x + it * gridDim.x;

@@ -54,6 +54,10 @@ struct AttnArgs {
   // sequences, writing one workspace slot per sequence piece
   // (partition_size is 0).
   int32_t split;
+  // Persistent partitioned launches (not split, no shared items) with two
+  // work groups on every CU: deal the plan's items over CUs rather than work
+  // groups (the kernel's item loop says how).  0: deal over work groups.
+  int32_t cu_deal;
   float scale_log2;    // scale * log2(e)
 };
 
