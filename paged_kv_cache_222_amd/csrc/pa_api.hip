@@ -145,6 +145,7 @@ hipError_t dispatch_attention(pa::AttnArgs a, int32_t dtype, int32_t d_head, int
   int64_t grid = rows * cols;
   a.persistent = 0;
   a.cu_deal = 0;
+  a.xcd_spread = 0;
   const DeviceFit fit = device_fit(dtype, d_head);
   const int64_t slots = (int64_t)fit.cus * fit.per_cu;
   if ((a.partition_size > 0 || a.split) && a.batch <= pa::kPlanBatch && slots >= cols) {
@@ -167,6 +168,7 @@ hipError_t dispatch_attention(pa::AttnArgs a, int32_t dtype, int32_t d_head, int
   // shared-prefix batch (31 items per work group) it cost 4 us at P 512.
   a.cu_deal = a.persistent && !a.split && a.prefix_parts == 0 && fit.per_cu == 2 &&
               grid == slots && (grid / cols) % 2 == 0;
+  a.xcd_spread = a.cu_deal && (grid / 2) % (8 * cols) == 0;
   if (grid > INT_MAX || cols > INT_MAX) {
     *status = PA_ERR_SHAPE;
     return hipSuccess;

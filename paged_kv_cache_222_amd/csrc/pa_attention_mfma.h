@@ -529,7 +529,23 @@ __global__ __launch_bounds__(kAttnThreads, PA_MFMA_MIN_BLOCKS) void attention_mf
   // to 143.9 us.  Other launches take every gridDim.x-th (item, column)
   // pair.
   const int W = plan ? (int)gridDim.x / K : 0;
-  const int jw = plan ? (int)blockIdx.x / K : 0;
+  // This work group's column and its index jw among the column's W work
+  // groups.  Blocks are dispatched to the eight XCDs round-robin (block b
+  // to XCD b % 8), so column = b % K keeps each column on one XCD.  With
+  // xcd_spread, block b = h * R + r (R = gridDim.x / 2, h the CU half)
+  // takes column (r / 8) % K and jw = h * R/K + (r / 8K) * 8 + r % 8: each
+  // column's work groups sit on all eight XCDs, and blocks b and b + R keep
+  // one column and slots jw and jw + W/2, as the CU deal needs.  On the
+  // LLaMA-3-8B batch every XCD then reads every KV head's tiles, and the
+  // launch went from 142.4-142.7 to 140.8-141.0 us (three alternating runs
+  // on one box; the odd XCDs stay the slower, by less).
+  int col_wg = plan ? (int)blockIdx.x % K : 0;
+  int jw = plan ? (int)blockIdx.x / K : 0;
+  if (plan && a.xcd_spread) {
+    const int R = (int)gridDim.x >> 1, r = (int)blockIdx.x % R, h = (int)blockIdx.x / R;
+    col_wg = (r >> 3) % K;
+    jw = h * (R / K) + (r / (8 * K)) * 8 + (r & 7);
+  }
   for (int it = 0;; ++it) {
     // ---- decode the item
     int kh, rr;
@@ -549,7 +565,7 @@ __global__ __launch_bounds__(kAttnThreads, PA_MFMA_MIN_BLOCKS) void attention_mf
       last_piece = (int64_t)Sb + Tb <= sp_hi;
       n_pieces = (Sb + Tb - 1) / sp_R - Sb / sp_R + 1;
     } else if (plan) {
-      kh = blockIdx.x % K;
+      kh = col_wg;
       if (a.cu_deal) {
         // round t of CU cu: position cu (t even) or C-1-cu (t odd); the
         // CU's first work group takes its even rounds, the second its odd

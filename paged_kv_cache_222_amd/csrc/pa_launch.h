@@ -58,6 +58,10 @@ struct AttnArgs {
   // work groups on every CU: deal the plan's items over CUs rather than work
   // groups (the kernel's item loop says how).  0: deal over work groups.
   int32_t cu_deal;
+  // With cu_deal, when half the grid is a multiple of 8 * columns: spread
+  // every column over the eight XCDs (see the kernel).  0: column =
+  // block % columns.
+  int32_t xcd_spread;
   float scale_log2;    // scale * log2(e)
 };
 
