@@ -123,7 +123,7 @@ def algorithmic_bytes(w):
 # form measured on MI355X for that batch (a batch with a shared prefix
 # reports "prefix").
 HEADLINE_FORM = {"llama3-8b": "fused", "qwen2.5-1.5b": "fused",
-                 "llama2-7b": "single", "tiny": "fused"}
+                 "llama2-7b": "partitioned", "tiny": "fused"}
 
 # sources whose change invalidates the HBM byte counts stored under profiles/
 KERNEL_SOURCES = ["pa_attention_mfma.h", "pa_attention_mfma.hip",

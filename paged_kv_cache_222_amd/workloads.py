@@ -180,9 +180,10 @@ CONFIGS: Dict[str, Config] = {
         name="llama2-7b", batch=32, n_q_heads=32, n_kv_heads=32, d_head=128,
         block_size=16, dtype="f16", max_context=4096,
         lengths=_constant(4096), std=0.5,
-        # not fixed by the workload: one partition per sequence was the
-        # fastest partitioned form (attention 339/340/345/349 us at
-        # 4096/2048/1024/512; the single pass is faster still, 331 us)
+        # not fixed by the workload: one partition per sequence is the
+        # fastest (fused step 329.7/332.2/337.6 us at 4096/2048/1024); the
+        # partitioned step, 327.0-329.3 us, is within ~1.5 % of the fused
+        # step and the single pass (329.8-334.4 us) on two MI355X boxes
         partition_size=4096,
         description="MHA 32/32 heads, d128, fp16, B=32, ctx 4096, "
                     "pool exactly B*L/16 blocks, values N(0, 0.5), "
