@@ -1,0 +1,80 @@
+"""Partitioned launches whose grid fills two work groups on every CU (rows x
+columns of at least the device's 512 slots of the d128 kernel), so the
+in-kernel plan deals its items over CUs and spreads each column over the
+eight XCDs, for 1 to 32 columns; 64 columns take the CU deal without the
+spread, and a d64 batch (three work groups per CU) neither.  Against the
+fp64 oracle through the C ABI (needs an MI355X): the folded-write step and
+pa_cache_write + pa_decode_partitioned, each followed by pa_reduce; every
+output element within the stated bound and the pools bit-exact after the
+write."""
+
+import numpy as np
+import pytest
+import torch
+
+from helpers import (DeviceBatch, as_f64, from_dev, note, oracle_out,
+                     oracle_pools_after_write, out_bound)
+from paged_kv_cache_222_amd import workloads as wl
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def pa():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import paged_kv_cache_222_amd as pa
+    pa.load()
+    return pa
+
+
+# (KV heads = columns, group size, batch, partition size, max context, dtype, D)
+SHAPES = [
+    (1, 8, 64, 32, 256, "bf16", 128),
+    (2, 4, 32, 32, 256, "f16", 128),
+    (4, 6, 32, 64, 256, "bf16", 128),
+    (8, 4, 16, 64, 256, "bf16", 128),
+    (16, 2, 8, 32, 128, "f16", 128),
+    (32, 1, 8, 64, 128, "bf16", 128),
+    (64, 1, 8, 128, 128, "f16", 128),
+    (8, 4, 24, 64, 256, "bf16", 64),
+]
+
+
+@pytest.mark.parametrize("shape", SHAPES, ids=lambda s: f"Hkv{s[0]}_G{s[1]}_B{s[2]}_P{s[3]}_{s[5]}_D{s[6]}")
+def test_full_grid_forms(pa, shape):
+    Hkv, G, B, P, max_ctx, dtype, D = shape
+    rng = np.random.default_rng(700 + Hkv + D)
+    ctx = [int(x) for x in rng.integers(1, max_ctx + 1, B)]
+    ctx[0] = max_ctx                       # the full number of partitions
+    pm = -(-max_ctx // P)
+    assert pm * B * Hkv >= 512             # the grid is the whole device (d128)
+    w = wl.make_custom(ctx, n_q_heads=Hkv * G, n_kv_heads=Hkv, d_head=D,
+                       block_size=16, dtype=dtype, seed=7000 + Hkv + D)
+    k_ref, v_ref = oracle_pools_after_write(w)
+    ref = oracle_out(w, k_ref, v_ref)
+    bound = out_bound(ref, dtype)
+    for form in ("step", "partitioned"):
+        note(f"full-grid {form}: Hkv{Hkv} G{G} B{B} P{P} ctx<={max_ctx} {dtype} D{D}")
+        d = DeviceBatch(w)
+        if form == "partitioned":
+            pa.pa_cache_write(d.key_new, d.value_new, d.k_pool, d.v_pool,
+                              d.slot_mapping)
+        ws = pa.partition_workspace(B, Hkv * G, D, pm)
+        for t in ws:
+            t.fill_(float("nan"))
+        if form == "step":
+            pa.pa_decode_step(*ws, d.key_new, d.value_new, d.q, d.k_pool,
+                              d.v_pool, d.block_table, d.context_lens,
+                              partition_size=P, scale=d.scale)
+        else:
+            pa.pa_decode_partitioned(*ws, d.q, d.k_pool, d.v_pool,
+                                     d.block_table, d.context_lens,
+                                     partition_size=P, scale=d.scale)
+        out = d.empty_out()
+        pa.pa_reduce(out, *ws, d.context_lens, partition_size=P)
+        torch.cuda.synchronize()
+        assert from_dev(d.k_pool).tobytes() == k_ref.tobytes(), form
+        assert from_dev(d.v_pool).tobytes() == v_ref.tobytes(), form
+        err = np.abs(as_f64(out) - ref)
+        assert (err <= bound).all(), (form, float(np.nanmax(err)))
