@@ -2,7 +2,8 @@
 of speculative decoding) + pa_reduce vs the fp64 oracle, through the C ABI
 (needs an MI355X).  Every output element within the stated max-abs-error on
 small ragged batches (sequences shorter than the token count included), on
-every row of the LLaMA-3-8B batch with 4 tokens, and the edge cases:
+chunks of 32 and 128 tokens per sequence (chunked prefill), on every row of
+the LLaMA-3-8B batch with 4 tokens, and the edge cases:
 one token equals pa_decode_partitioned bit for bit, and a partition beyond a
 token's causal limit is written as empty."""
 
@@ -71,6 +72,28 @@ def test_multi_query_small(pa, dtype, D, BS, Hkv, G, k, P):
     err = np.abs(got - ref)
     print(f"{dtype} D{D} BS{BS} G{G} k{k} P{P}: max err {err.max():.3g}")
     assert (err <= bound).all()
+
+
+# chunked prefill: a chunk of k new tokens per sequence, causal among
+# themselves (the whole sequence when ctx == k); G * k columns per KV head
+# in 8 and 64 chunks of 16
+CHUNKS = [  # dtype, D, BS, Hkv, G, k, P, contexts
+    ("bf16", 128, 16, 2, 4, 32, 256, [32, 33, 100, 500, 1000]),
+    ("f16", 64, 16, 1, 8, 128, 512, [128, 200, 700, 1500])]
+
+
+@pytest.mark.parametrize("dtype,D,BS,Hkv,G,k,P,ctx", CHUNKS)
+def test_chunked_prefill(pa, dtype, D, BS, Hkv, G, k, P, ctx):
+    w = wl.make_custom(ctx, n_q_heads=Hkv * G, n_kv_heads=Hkv, d_head=D,
+                       block_size=BS, dtype=dtype, seed=k)
+    k_ref, v_ref = oracle_pools_after_write(w)
+    qm = wl.make_multi_queries(w, k, seed=k)
+    out, _ = run_multi(pa, w, qm, k_ref, v_ref, P, f"chunk {dtype} D{D} G{G}")
+    ref = oracle.oracle_decode_multi(qm, k_ref, v_ref, w.block_table,
+                                     w.context_lens, w.scale, G, BS, dtype)
+    err = np.abs(as_f64(out) - ref)
+    print(f"chunked prefill {dtype} D{D} G{G} k{k} P{P}: max err {err.max():.3g}")
+    assert (err <= out_bound(ref, dtype)).all()
 
 
 def test_multi_query_llama3_every_row(pa):
