@@ -2,7 +2,8 @@
 columns of at least the device's 512 slots of the d128 kernel), so the
 in-kernel plan deals its items over CUs and spreads each column over the
 eight XCDs, for 1 to 32 columns; 64 columns take the CU deal without the
-spread, and a d64 batch (three work groups per CU) neither.  Against the
+spread, and a d64 batch (three work groups per CU) neither; and the plan's
+largest batch, 1,024 sequences, and one more.  Against the
 fp64 oracle through the C ABI (needs an MI355X): the folded-write step and
 pa_cache_write + pa_decode_partitioned, each followed by pa_reduce; every
 output element within the stated bound and the pools bit-exact after the
@@ -61,6 +62,46 @@ def test_full_grid_forms(pa, shape):
             pa.pa_cache_write(d.key_new, d.value_new, d.k_pool, d.v_pool,
                               d.slot_mapping)
         ws = pa.partition_workspace(B, Hkv * G, D, pm)
+        for t in ws:
+            t.fill_(float("nan"))
+        if form == "step":
+            pa.pa_decode_step(*ws, d.key_new, d.value_new, d.q, d.k_pool,
+                              d.v_pool, d.block_table, d.context_lens,
+                              partition_size=P, scale=d.scale)
+        else:
+            pa.pa_decode_partitioned(*ws, d.q, d.k_pool, d.v_pool,
+                                     d.block_table, d.context_lens,
+                                     partition_size=P, scale=d.scale)
+        out = d.empty_out()
+        pa.pa_reduce(out, *ws, d.context_lens, partition_size=P)
+        torch.cuda.synchronize()
+        assert from_dev(d.k_pool).tobytes() == k_ref.tobytes(), form
+        assert from_dev(d.v_pool).tobytes() == v_ref.tobytes(), form
+        err = np.abs(as_f64(out) - ref)
+        assert (err <= bound).all(), (form, float(np.nanmax(err)))
+
+
+@pytest.mark.parametrize("B", [1024, 1025])
+def test_plan_batch_limits(pa, B):
+    """The in-kernel plan's largest batch (1024 sequences: ranks over 1024
+    keys, items dealt over CUs, columns spread over the XCDs) and one more
+    (no plan: a work group per (row, column) pair), short ragged contexts."""
+    rng = np.random.default_rng(B)
+    ctx = [int(x) for x in rng.integers(1, 201, B)]
+    P = 64
+    pm = -(-max(ctx) // P)
+    w = wl.make_custom(ctx, n_q_heads=8, n_kv_heads=2, d_head=128,
+                       block_size=16, dtype="bf16", seed=B)
+    k_ref, v_ref = oracle_pools_after_write(w)
+    ref = oracle_out(w, k_ref, v_ref)
+    bound = out_bound(ref, "bf16")
+    for form in ("step", "partitioned"):
+        note(f"plan batch limit {form}: B{B} P{P} PMAX{pm}")
+        d = DeviceBatch(w)
+        if form == "partitioned":
+            pa.pa_cache_write(d.key_new, d.value_new, d.k_pool, d.v_pool,
+                              d.slot_mapping)
+        ws = pa.partition_workspace(B, 8, 128, pm)
         for t in ws:
             t.fill_(float("nan"))
         if form == "step":
