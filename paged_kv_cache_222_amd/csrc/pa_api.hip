@@ -164,11 +164,13 @@ hipError_t dispatch_attention(pa::AttnArgs a, int32_t dtype, int32_t d_head, int
     a.prefix_seqs = 0;
   }
   // Items dealt over CUs: the grid fills two work groups on every CU and a
-  // CU's two work groups are in one column.  Not with shared items: on the
-  // shared-prefix batch (31 items per work group) it cost 4 us at P 512.
-  a.cu_deal = a.persistent && !a.split && a.prefix_parts == 0 && fit.per_cu == 2 &&
-              grid == slots && (grid / cols) % 2 == 0;
-  a.xcd_spread = a.cu_deal && (grid / 2) % (8 * cols) == 0;
+  // CU's two work groups are in one column.  With shared items a CU's work
+  // groups take pairs of rounds, and the columns stay on their XCDs (there
+  // each XCD's L2 holds its column's prefix tiles).
+  const bool cu_fit = a.persistent && !a.split && fit.per_cu == 2 && grid == slots &&
+                      (grid / cols) % 2 == 0;
+  a.cu_deal = cu_fit ? (a.prefix_parts > 0 ? 2 : 1) : 0;
+  a.xcd_spread = a.cu_deal == 1 && (grid / 2) % (8 * cols) == 0;
   if (grid > INT_MAX || cols > INT_MAX) {
     *status = PA_ERR_SHAPE;
     return hipSuccess;

@@ -567,9 +567,17 @@ __global__ __launch_bounds__(kAttnThreads, PA_MFMA_MIN_BLOCKS) void attention_mf
     } else if (plan) {
       kh = col_wg;
       if (a.cu_deal) {
-        // round t of CU cu: position cu (t even) or C-1-cu (t odd); the
-        // CU's first work group takes its even rounds, the second its odd
-        const int C = W >> 1, cu = jw % C, t = 2 * it + jw / C;
+        // round t of CU cu: position cu (t even) or C-1-cu (t odd).  The
+        // CU's first work group takes its even rounds and the second its odd
+        // ones; or (cu_deal 2) the first takes rounds 0, 1, 4, 5, ... and the
+        // second 2, 3, 6, 7, ...: with shared items the list alternates
+        // shared and private items, and alternating single rounds would give
+        // one work group of a CU only shared items and the other only
+        // private ones (shared-prefix batch, P 512: 612.0/612.3 us that way,
+        // 606.7/608.6 with the work-group deal, 604.3/605.2 with pairs of
+        // rounds)
+        const int C = W >> 1, cu = jw % C, h = jw / C;
+        const int t = a.cu_deal == 2 ? 4 * (it >> 1) + 2 * h + (it & 1) : 2 * it + h;
         rr = t * C + ((t & 1) ? C - 1 - cu : cu);
       } else {
         rr = it * W + ((it & 1) ? W - 1 - jw : jw);

@@ -54,11 +54,14 @@ struct AttnArgs {
   // sequences, writing one workspace slot per sequence piece
   // (partition_size is 0).
   int32_t split;
-  // Persistent partitioned launches (not split, no shared items) with two
-  // work groups on every CU: deal the plan's items over CUs rather than work
-  // groups (the kernel's item loop says how).  0: deal over work groups.
+  // Persistent partitioned launches (not split) with two work groups on
+  // every CU: deal the plan's items over CUs rather than work groups (the
+  // kernel's item loop says how).  0: deal over work groups; 1: a CU's
+  // rounds alternate between its two work groups; 2: pairs of rounds do
+  // (launches with shared items, whose list alternates shared and private
+  // items).
   int32_t cu_deal;
-  // With cu_deal, when half the grid is a multiple of 8 * columns: spread
+  // With cu_deal 1, when half the grid is a multiple of 8 * columns: spread
   // every column over the eight XCDs (see the kernel).  0: column =
   // block % columns.
   int32_t xcd_spread;
