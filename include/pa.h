@@ -17,9 +17,9 @@
  * ---------------------------------
  * - Pointers are DEVICE pointers owned by the caller unless stated otherwise.
  *   The GPU entry points never allocate or free memory.  State they keep:
- *   a note of how many work groups fit on each of the first 64 devices
- *   (filled on first use, thread-safe; later devices are queried on every
- *   call); the fixed device array of pa_decode_step_noalloc (one per device,
+ *   a note of each of the first 64 devices' CU count and of how many work
+ *   groups of the attention kernel fit on one CU (filled on first use,
+ *   thread-safe; later devices are queried on every call); the fixed device array of pa_decode_step_noalloc (one per device,
  *   shared by that entry point's calls, see there); and the two events set
  *   by pa_time_next_attention, per host thread, until the launch that uses
  *   them.  Apart from pa_decode_step_noalloc, calls on different streams or
