@@ -5,6 +5,7 @@ the number of resident input copies, and the lookup of stored HBM counters
 change)."""
 
 import os
+import re
 import sys
 
 import numpy as np
@@ -65,3 +66,37 @@ def test_traffic_lookup_matches_form_and_sources(monkeypatch):
     assert bench.measured_traffic("no-such-batch", "fused", 3072, 16) is None
     monkeypatch.setattr(bench, "kernel_source_hash", lambda: "0" * 16)
     assert bench.measured_traffic("llama3-8b", "fused", 3072, 16) is None
+
+
+@pytest.mark.parametrize("name,form,P", [
+    ("llama3-8b", "fused", 3072), ("qwen2.5-1.5b", "fused", 1536),
+    ("llama2-7b", "partitioned", 4096), ("shared-prefix", "prefix", 512)])
+def test_every_headline_form_has_counters(name, form, P):
+    """Each batch's reported form has HBM counters under profiles/ for its
+    partition size, so the bench line can carry them; when the kernel
+    sources still match the ones they were taken on, the traffic is within
+    a few percent of the algorithmic bytes stated beside it."""
+    if name in bench.HEADLINE_FORM:
+        assert bench.HEADLINE_FORM[name] == form
+    found = None
+    for fname in os.listdir(os.path.join(ROOT, "profiles")):
+        if not fname.endswith("_hbm_counters.txt") or f"_{name}_" not in fname:
+            continue
+        kv = {}
+        text = open(os.path.join(ROOT, "profiles", fname)).read()
+        for line in text.splitlines():
+            if ":" in line and not line.startswith("#"):
+                k, v = line.split(":", 1)
+                kv[k.strip()] = v.strip()
+        if kv.get("variant") == form and kv.get("partition_size") == str(P):
+            m = re.search(r"Algorithmic bytes per launch \(bench.py's figure for this "
+                          r"launch\) are (\d+)", " ".join(text.split()))
+            found = (kv, int(m.group(1)) if m else None)
+    assert found is not None, f"no counters for {name} {form} P{P}"
+    kv, alg = found
+    got = bench.measured_traffic(name, form, P, int(kv["block_size"]))
+    if kv["source_sha256_16"] == bench.kernel_source_hash():
+        assert got is not None and alg is not None
+        assert 1.0 <= got / alg < 1.03, (name, got / alg)
+    else:
+        assert got is None
