@@ -171,8 +171,8 @@ CONFIGS: Dict[str, Config] = {
         name="qwen2.5-1.5b", batch=64, n_q_heads=12, n_kv_heads=2, d_head=128,
         block_size=16, dtype="bf16", max_context=4096,
         lengths=_uniform(128, 4096), pool_blocks=20000,
-        # not fixed by the workload: among 256..2048 on MI355X, 640 and
-        # 1536 were fastest (attention 33.8 us against 36.7 at 2048)
+        # not fixed by the workload: among 256..2048 on MI355X, 1536 is the
+        # fastest (attention 33.6-33.8 us; 34.0-34.3 at 640, 35.5-35.7 at 768)
         partition_size=1536,
         description="12/2 heads, d128, bf16, B=64, ctx U[128,4096], "
                     "20k-block pool, 1536-token partitions"),
@@ -192,8 +192,8 @@ CONFIGS: Dict[str, Config] = {
         name="llama3-8b", batch=128, n_q_heads=32, n_kv_heads=8, d_head=128,
         block_size=16, dtype="bf16", max_context=8192,
         lengths=_lognormal(1024, 1.0, 16, 8192),
-        # not fixed by the workload: the fastest of 1536..4096 on MI355X
-        # (step 155.7/151.4/153.4/147.5/152.8 us at 1536/2048/2560/3072/4096)
+        # not fixed by the workload: the fastest of 2048..4096 on MI355X
+        # (step 148.8/152.5/146.7/147.8/149.6 us at 2048/2560/3072/3584/4096)
         partition_size=3072,
         description="GQA 32/8 heads, d128, bf16, B=128, ctx log-normal "
                     "(median 1024, sigma 1) clipped to [16, 8192], "
